@@ -1,0 +1,212 @@
+/*
+ * pkv.h - C ABI of libpkv.so: the PagedAttention hot path on AMD MI355X (gfx950).
+ *
+ * Keys and values of every sequence live in fixed-size blocks of one physical
+ * pool.  Each sequence finds its blocks through a per-sequence block table that
+ * maps logical block j to a physical block id.  The blocks need not be
+ * contiguous or ordered, and several sequences may reference the same physical
+ * block.  Sources:
+ *   "PagedAttention and vLLM, annotated", sections 4.1-4.2
+ *   "vLLM & PagedAttention: Efficient Memory Management for LLM Serving",
+ *   sections III, V and X
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - Every array argument is a DEVICE pointer to memory the caller owns and keeps
+ *    alive until the work on `stream` has finished.  The library allocates
+ *    nothing and keeps no state between calls.  Arrays are dense (row-major,
+ *    no padding) and 16-byte aligned.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).  Every
+ *    call only enqueues work and returns without synchronising.  Two calls are
+ *    ordered exactly when they are ordered on their streams.
+ *  - Sizes and maxima that size a launch grid (num_tokens, num_seqs,
+ *    max_context_len, num_prompts, max_prompt_len, total_tokens) come from the
+ *    host, so no call ever reads device memory back.
+ *  - Return value: PKV_OK, or a negative pkv_status.  No call aborts, throws or
+ *    prints.  On error nothing is enqueued.  The one exception is PKV_ELAUNCH,
+ *    where a kernel may already be queued.  A fault inside a kernel (for example
+ *    an index the caller promised was valid) shows up at the caller's next
+ *    synchronisation, as HIP reports it.
+ *  - Element types: pkv_dtype.  bf16 is the upper half of an IEEE float32.
+ *  - Set PKV_VALIDATE=1 in the environment to make each call copy its index
+ *    arrays to the host and check them before launching: table entries in
+ *    range, context lengths in [1, max_context_len], slots unique and in range.
+ *    This mode synchronises the stream; it is for tests.  A failed check
+ *    returns PKV_EINVAL.
+ *
+ * KV pool layout (both k_cache and v_cache)
+ * -----------------------------------------
+ *    [num_blocks][num_heads][block_size][head_dim]
+ *  One (block, head) tile holds block_size tokens x head_dim values,
+ *  contiguously: 4 KiB for 16 x 128 x 2 B.  A decode wavefront reads it as one
+ *  fully coalesced 4 KiB burst.  Physical block b with offset o is slot
+ *  b * block_size + o.  One block table per sequence is shared by all heads of
+ *  the layer: a physical id names the same block index in every head's slice.
+ *
+ * Supported: block_size 16; head_dim 64 or 128; dtype f32, f16 or bf16 for the
+ * write and decode; f16 or bf16 for prefill.  Output dtype: f32, or the input
+ * dtype.  Accumulation is always in f32, and the result is rounded once
+ * (nearest-even) when stored.
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { PKV_F32 = 0, PKV_F16 = 1, PKV_BF16 = 2 } pkv_dtype;
+
+typedef enum {
+  PKV_OK = 0,
+  PKV_EINVAL = -1,     /* null pointer, bad size, misaligned pointer, failed PKV_VALIDATE check */
+  PKV_ENOTSUP = -2,    /* block_size / head_dim / dtype combination not built, or device not gfx950 */
+  PKV_ELAUNCH = -3,    /* the HIP runtime reported an error when launching */
+  PKV_EDEVICE = -4,    /* the HIP runtime failed to report the current device */
+  PKV_EWORKSPACE = -5  /* workspace smaller than pkv_decode_workspace_bytes() asks for */
+} pkv_status;
+
+/* Shape and element type of a KV pool (k_cache and v_cache share it). */
+typedef struct {
+  int64_t num_blocks; /* physical blocks in the pool */
+  int32_t num_heads;  /* heads per layer (query heads = KV heads) */
+  int32_t head_dim;   /* values per head */
+  int32_t block_size; /* tokens per block */
+  int32_t dtype;      /* pkv_dtype of the stored keys/values */
+} pkv_cache_desc;
+
+/* Version of this ABI; bumped on any incompatible change. */
+int pkv_abi_version(void);
+
+/* Static string naming a status code. */
+const char* pkv_status_str(int status);
+
+/* PKV_OK when the current HIP device is a gfx950 (MI355X); PKV_ENOTSUP or PKV_EDEVICE otherwise. */
+int pkv_check_device(void);
+
+/*
+ * pkv_kv_cache_write - scatter new tokens' keys and values into their slots.
+ *
+ * Writes the K/V of the current tokens into the physical blocks that the block
+ * tables assign to them, as one fused reshape-and-write kernel ("vLLM &
+ * PagedAttention ...", section X, first kernel detail).  Prompt tokens fill
+ * logical blocks left to right; a decode token goes to the next free slot of
+ * its last block (same page, section V, Figure 6).
+ *
+ *   k, v          [num_tokens][num_heads][head_dim], desc->dtype
+ *   slot_mapping  int64 [num_tokens]: destination slot of each token.  slot < 0
+ *                 means "padding, skip".  A slot >= num_blocks*block_size is
+ *                 skipped too, so a bad slot never writes out of bounds.
+ *                 Slots must be unique within one call; with duplicates, which
+ *                 token lands is unspecified.
+ *   k_cache, v_cache  the pool (layout above), modified in place.
+ * For every token t and head h with a valid slot:
+ *   cache[slot / block_size][h][slot % block_size][:] = new[t][h][:]
+ * The copy is byte-exact, with no conversion.  No other byte of the pool changes.
+ * num_tokens == 0 is a no-op.
+ */
+int pkv_kv_cache_write(const void* k, const void* v, const int64_t* slot_mapping, int64_t num_tokens,
+                       void* k_cache, void* v_cache, const pkv_cache_desc* desc, void* stream);
+
+/*
+ * Workspace for pkv_paged_attn_decode: partial results of the split-context
+ * decode, in float32.  num_seqs * num_heads * P * (head_dim + 2) * 4 bytes,
+ * where P = ceil(max_context_len / partition_size).  The size is 0 when
+ * partition_size == 0 (no split) or no sequence can span two partitions.
+ */
+size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                                  int32_t max_context_len, int32_t partition_size);
+
+/*
+ * pkv_paged_attn_decode - attention of each sequence's current token over its
+ * whole cached context, gathered block by block through its block table.
+ *
+ * Computes exactly ordinary softmax attention
+ *   out[s][h] = sum_t softmax_t(scale * q[s][h] . k_t) v_t,  t = 0 .. context_lens[s]-1
+ * ("vLLM & PagedAttention ...", section I, attention equation, with i the last
+ * position).  It is evaluated block by block (section III, block-wise equation),
+ * with a running normaliser across blocks ("PagedAttention and vLLM, annotated",
+ * section 4.1).  context_lens[s] includes the current token, so that token's
+ * K/V must already be in the pool.  Slots at or past the context length are
+ * never used, whatever they hold (NaN included).  Table entries past the last
+ * used block are never read.
+ *
+ *   q             [num_seqs][num_heads][head_dim], desc->dtype
+ *   k_cache, v_cache  the pool (read only)
+ *   block_tables  int32 [num_seqs][max_blocks_per_seq] physical ids
+ *   context_lens  int32 [num_seqs], each in [1, max_context_len];
+ *                 max_context_len <= max_blocks_per_seq * block_size
+ *   scale         multiplies q.k before the softmax (usually 1/sqrt(head_dim))
+ *   out           [num_seqs][num_heads][head_dim] of out_dtype (PKV_F32 or desc->dtype)
+ *   partition_size  tokens per context partition, a multiple of 16 between 16 and
+ *                 4096, or 0 for no split.  Each (sequence, head, partition)
+ *                 is one workgroup.  A sequence spanning more than one partition
+ *                 is merged by a second, reduce kernel (max-rescaled sum of the
+ *                 partial results), in a fixed order.
+ *   workspace     device scratch of at least pkv_decode_workspace_bytes(...)
+ *                 (may be NULL when that is 0).  The caller owns it.  Calls that
+ *                 run at the same time need separate workspaces.
+ * Results are deterministic: no atomics, and the merge order is fixed.  The
+ * output does not depend on which physical ids hold the blocks, or on whether
+ * blocks are shared.  A table entry outside [0, num_blocks) makes that
+ * sequence's output NaN instead of reading out of bounds.
+ */
+int pkv_paged_attn_decode(const void* q, const void* k_cache, const void* v_cache, const pkv_cache_desc* desc,
+                          const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                          int32_t num_seqs, int32_t max_context_len, float scale, void* out, int32_t out_dtype,
+                          int32_t partition_size, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The two stages of pkv_paged_attn_decode, exposed so a caller can time or
+ * overlap them.  The arguments are identical.  _partial launches the
+ * per-partition kernel.  It writes `out` for sequences that fit one partition,
+ * and the workspace for the others.  _reduce then merges the workspace into
+ * `out`.  _partial followed by _reduce on one stream is the whole of
+ * pkv_paged_attn_decode, bit for bit.
+ */
+int pkv_paged_attn_decode_partial(const void* q, const void* k_cache, const void* v_cache,
+                                  const pkv_cache_desc* desc, const int32_t* block_tables,
+                                  int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
+                                  int32_t max_context_len, float scale, void* out, int32_t out_dtype,
+                                  int32_t partition_size, void* workspace, size_t workspace_bytes, void* stream);
+int pkv_paged_attn_decode_reduce(const void* q, const void* k_cache, const void* v_cache,
+                                 const pkv_cache_desc* desc, const int32_t* block_tables,
+                                 int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
+                                 int32_t max_context_len, float scale, void* out, int32_t out_dtype,
+                                 int32_t partition_size, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * pkv_paged_attn_prefill - causal self-attention over each prompt (prompt phase).
+ *
+ * All positions of a prompt are known at once, so this is dense matrix-matrix
+ * attention: S = scale * Q K^T masked to key <= query, a row softmax, then
+ * O = P V ("vLLM & PagedAttention ...", section I: the prompt phase and the t <= i
+ * limit of the attention equation).  It runs on the MFMA matrix cores, with
+ * fp32 accumulation.
+ *
+ *   q, k, v        packed prompts [total_tokens][num_heads][head_dim] of `dtype`
+ *                  (PKV_F16 or PKV_BF16).  Prompt p occupies rows
+ *                  off_p .. off_p + prompt_lens[p] - 1, off_p = sum of earlier lengths.
+ *   block_tables   int32 [num_prompts][max_blocks_per_seq] or NULL.  Reserved.
+ *                  Prefill attends over the contiguous k, v above.  After
+ *                  pkv_kv_cache_write those hold the same bytes as the
+ *                  prompt's blocks, so the result is the same either way.
+ *   prompt_lens    int32 [num_prompts], each in [0, max_prompt_len]; their sum
+ *                  must equal total_tokens.  Rows beyond total_tokens are never
+ *                  touched.
+ *   scale          multiplies q.k (usually 1/sqrt(head_dim))
+ *   out            [total_tokens][num_heads][head_dim] of out_dtype (PKV_F32 or `dtype`)
+ */
+int pkv_paged_attn_prefill(const void* q, const void* k, const void* v, int32_t num_heads, int32_t head_dim,
+                           int32_t dtype, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                           const int32_t* prompt_lens, int32_t num_prompts, int64_t total_tokens,
+                           int32_t max_prompt_len, float scale, void* out, int32_t out_dtype, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

@@ -1,0 +1,294 @@
+// C ABI of libpkv (declared in include/pkv.h): argument checks, dtype/shape
+// dispatch to the gfx950 kernels, and mapping HIP launch errors to status codes.
+// Nothing here allocates device memory, and nothing synchronises, except the
+// PKV_VALIDATE=1 mode, which copies index arrays to the host to check them.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdlib>
+#include <cstring>
+#include <vector>
+
+#include "pkv.h"
+#include "pkv_internal.h"
+
+namespace {
+
+constexpr int kAbiVersion = 1;
+constexpr int kBlock = 16;
+constexpr int kMaxDevices = 64;
+int g_arch[kMaxDevices];  // 0 = not yet checked, 1 = gfx950, -1 = other
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+bool valid_dtype(int d) { return d == PKV_F32 || d == PKV_F16 || d == PKV_BF16; }
+
+bool validate_mode() {
+  static const bool on = [] {
+    const char* e = std::getenv("PKV_VALIDATE");
+    return e != nullptr && e[0] != '\0' && e[0] != '0';
+  }();
+  return on;
+}
+
+int device_status() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return PKV_EDEVICE;
+  if (dev < kMaxDevices && g_arch[dev] != 0) return g_arch[dev] > 0 ? PKV_OK : PKV_ENOTSUP;
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return PKV_EDEVICE;
+  const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  if (dev < kMaxDevices) g_arch[dev] = ok ? 1 : -1;
+  return ok ? PKV_OK : PKV_ENOTSUP;
+}
+
+int check_desc(const pkv_cache_desc* d) {
+  if (d == nullptr) return PKV_EINVAL;
+  if (d->num_blocks <= 0 || d->num_heads <= 0 || d->head_dim <= 0 || d->block_size <= 0) return PKV_EINVAL;
+  if (!valid_dtype(d->dtype)) return PKV_EINVAL;
+  if (d->block_size != kBlock) return PKV_ENOTSUP;
+  if (d->head_dim != 64 && d->head_dim != 128) return PKV_ENOTSUP;
+  return PKV_OK;
+}
+
+int launch_status(hipError_t e) { return e == hipSuccess ? PKV_OK : PKV_ELAUNCH; }
+
+template <typename T>
+bool copy_to_host(std::vector<T>& dst, const T* src, size_t n, hipStream_t st) {
+  dst.resize(n);
+  if (n == 0) return true;
+  if (hipMemcpyAsync(dst.data(), src, n * sizeof(T), hipMemcpyDeviceToHost, st) != hipSuccess) return false;
+  return hipStreamSynchronize(st) == hipSuccess;
+}
+
+struct DecodePlan {
+  int32_t part_blocks = 0;
+  int32_t num_parts = 0;
+  size_t ws_bytes = 0;
+};
+
+DecodePlan plan_decode(int32_t num_seqs, int32_t num_heads, int32_t head_dim, int32_t max_context_len,
+                       int32_t partition_size) {
+  DecodePlan p;
+  if (partition_size == 0) {
+    p.part_blocks = (max_context_len + kBlock - 1) / kBlock;
+    p.num_parts = 1;
+  } else {
+    p.part_blocks = partition_size / kBlock;
+    p.num_parts = (max_context_len + partition_size - 1) / partition_size;
+  }
+  if (p.num_parts > 1)
+    p.ws_bytes = (size_t)num_seqs * num_heads * p.num_parts * ((size_t)head_dim + 2) * sizeof(float);
+  return p;
+}
+
+enum Stage { kPartial = 1, kReduce = 2, kBoth = 3 };
+
+int decode_impl(int stages, const void* q, const void* k_cache, const void* v_cache, const pkv_cache_desc* desc,
+                const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                int32_t num_seqs, int32_t max_context_len, float scale, void* out, int32_t out_dtype,
+                int32_t partition_size, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_desc(desc);
+  if (st != PKV_OK) return st;
+  if (num_seqs < 0 || max_blocks_per_seq <= 0 || max_context_len <= 0) return PKV_EINVAL;
+  if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * kBlock) return PKV_EINVAL;
+  if (out_dtype != PKV_F32 && out_dtype != desc->dtype) return PKV_ENOTSUP;
+  if (partition_size != 0 && (partition_size % kBlock != 0 || partition_size < kBlock || partition_size > 4096))
+    return PKV_EINVAL;
+  if (num_seqs == 0) return PKV_OK;
+  if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out) return PKV_EINVAL;
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16)) return PKV_EINVAL;
+  if (!aligned(block_tables, 4) || !aligned(context_lens, 4)) return PKV_EINVAL;
+  const DecodePlan plan = plan_decode(num_seqs, desc->num_heads, desc->head_dim, max_context_len, partition_size);
+  const int64_t units = (int64_t)num_seqs * desc->num_heads * plan.num_parts;
+  if (units > ((int64_t)1 << 31) - 64 || num_seqs > 65535 * 32768) return PKV_EINVAL;
+  if (desc->num_heads > 65535) return PKV_EINVAL;
+  if (plan.ws_bytes > 0) {
+    if (workspace == nullptr || !aligned(workspace, 16)) return PKV_EINVAL;
+    if (workspace_bytes < plan.ws_bytes) return PKV_EWORKSPACE;
+  }
+  st = device_status();
+  if (st != PKV_OK) return st;
+  hipStream_t sm = reinterpret_cast<hipStream_t>(stream);
+
+  if (validate_mode()) {
+    std::vector<int32_t> lens, tab;
+    if (!copy_to_host(lens, context_lens, (size_t)num_seqs, sm)) return PKV_EDEVICE;
+    if (!copy_to_host(tab, block_tables, (size_t)num_seqs * max_blocks_per_seq, sm)) return PKV_EDEVICE;
+    for (int32_t s = 0; s < num_seqs; ++s) {
+      if (lens[s] < 1 || lens[s] > max_context_len) return PKV_EINVAL;
+      const int32_t nb = (lens[s] + kBlock - 1) / kBlock;
+      for (int32_t j = 0; j < nb; ++j) {
+        const int32_t b = tab[(size_t)s * max_blocks_per_seq + j];
+        if (b < 0 || b >= desc->num_blocks) return PKV_EINVAL;
+      }
+    }
+  }
+
+  pkv::DecodeArgs a{};
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.out = out;
+  a.ws_acc = reinterpret_cast<float*>(workspace);
+  a.ws_ml = plan.ws_bytes ? a.ws_acc + (size_t)num_seqs * desc->num_heads * plan.num_parts * desc->head_dim : nullptr;
+  a.num_blocks = desc->num_blocks;
+  a.num_heads = desc->num_heads;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.num_seqs = num_seqs;
+  a.max_context_len = max_context_len;
+  a.part_blocks = plan.part_blocks;
+  a.num_parts = plan.num_parts;
+  a.total_units = (int32_t)units;
+  a.per_xcd = (int32_t)((units + 7) / 8);
+  a.scale_log2 = scale * 1.4426950408889634f;
+
+  if (stages & kPartial) {
+    st = launch_status(pkv::launch_decode_partial(a, desc->dtype, out_dtype, desc->head_dim, sm));
+    if (st != PKV_OK) return st;
+  }
+  if ((stages & kReduce) && plan.num_parts > 1) {
+    st = launch_status(pkv::launch_decode_reduce(a, out_dtype, desc->head_dim, sm));
+    if (st != PKV_OK) return st;
+  }
+  return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pkv_abi_version(void) { return kAbiVersion; }
+
+const char* pkv_status_str(int status) {
+  switch (status) {
+    case PKV_OK: return "ok";
+    case PKV_EINVAL: return "invalid argument";
+    case PKV_ENOTSUP: return "not supported (block size, head dim, dtype or device)";
+    case PKV_ELAUNCH: return "kernel launch failed";
+    case PKV_EDEVICE: return "HIP device query failed";
+    case PKV_EWORKSPACE: return "workspace too small";
+    default: return "unknown status";
+  }
+}
+
+int pkv_check_device(void) { return device_status(); }
+
+int pkv_kv_cache_write(const void* k, const void* v, const int64_t* slot_mapping, int64_t num_tokens, void* k_cache,
+                       void* v_cache, const pkv_cache_desc* desc, void* stream) {
+  int st = check_desc(desc);
+  if (st != PKV_OK) return st;
+  if (num_tokens < 0) return PKV_EINVAL;
+  if (num_tokens == 0) return PKV_OK;
+  if (!k || !v || !slot_mapping || !k_cache || !v_cache) return PKV_EINVAL;
+  if (!aligned(k, 16) || !aligned(v, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(slot_mapping, 8))
+    return PKV_EINVAL;
+  st = device_status();
+  if (st != PKV_OK) return st;
+  hipStream_t sm = reinterpret_cast<hipStream_t>(stream);
+  if (validate_mode()) {
+    std::vector<int64_t> slots;
+    if (!copy_to_host(slots, slot_mapping, (size_t)num_tokens, sm)) return PKV_EDEVICE;
+    std::vector<int64_t> used;
+    used.reserve(slots.size());
+    for (int64_t x : slots) {
+      if (x < 0) continue;
+      if (x >= desc->num_blocks * kBlock) return PKV_EINVAL;
+      used.push_back(x);
+    }
+    std::sort(used.begin(), used.end());
+    if (std::adjacent_find(used.begin(), used.end()) != used.end()) return PKV_EINVAL;
+  }
+  pkv::WriteArgs a{};
+  a.k = k;
+  a.v = v;
+  a.slot_mapping = slot_mapping;
+  a.num_tokens = num_tokens;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.num_blocks = desc->num_blocks;
+  a.num_heads = desc->num_heads;
+  a.head_dim = desc->head_dim;
+  a.dtype = desc->dtype;
+  return launch_status(pkv::launch_kv_cache_write(a, sm));
+}
+
+size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim, int32_t max_context_len,
+                                  int32_t partition_size) {
+  if (num_seqs <= 0 || num_heads <= 0 || head_dim <= 0 || max_context_len <= 0 || partition_size < 0) return 0;
+  if (partition_size != 0 && partition_size % kBlock != 0) return 0;
+  return plan_decode(num_seqs, num_heads, head_dim, max_context_len, partition_size).ws_bytes;
+}
+
+int pkv_paged_attn_decode(const void* q, const void* k_cache, const void* v_cache, const pkv_cache_desc* desc,
+                          const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                          int32_t num_seqs, int32_t max_context_len, float scale, void* out, int32_t out_dtype,
+                          int32_t partition_size, void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_impl(kBoth, q, k_cache, v_cache, desc, block_tables, max_blocks_per_seq, context_lens, num_seqs,
+                     max_context_len, scale, out, out_dtype, partition_size, workspace, workspace_bytes, stream);
+}
+
+int pkv_paged_attn_decode_partial(const void* q, const void* k_cache, const void* v_cache,
+                                  const pkv_cache_desc* desc, const int32_t* block_tables,
+                                  int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
+                                  int32_t max_context_len, float scale, void* out, int32_t out_dtype,
+                                  int32_t partition_size, void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_impl(kPartial, q, k_cache, v_cache, desc, block_tables, max_blocks_per_seq, context_lens, num_seqs,
+                     max_context_len, scale, out, out_dtype, partition_size, workspace, workspace_bytes, stream);
+}
+
+int pkv_paged_attn_decode_reduce(const void* q, const void* k_cache, const void* v_cache,
+                                 const pkv_cache_desc* desc, const int32_t* block_tables,
+                                 int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
+                                 int32_t max_context_len, float scale, void* out, int32_t out_dtype,
+                                 int32_t partition_size, void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_impl(kReduce, q, k_cache, v_cache, desc, block_tables, max_blocks_per_seq, context_lens, num_seqs,
+                     max_context_len, scale, out, out_dtype, partition_size, workspace, workspace_bytes, stream);
+}
+
+int pkv_paged_attn_prefill(const void* q, const void* k, const void* v, int32_t num_heads, int32_t head_dim,
+                           int32_t dtype, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                           const int32_t* prompt_lens, int32_t num_prompts, int64_t total_tokens,
+                           int32_t max_prompt_len, float scale, void* out, int32_t out_dtype, void* stream) {
+  if (dtype != PKV_F16 && dtype != PKV_BF16) return valid_dtype(dtype) ? PKV_ENOTSUP : PKV_EINVAL;
+  if (out_dtype != PKV_F32 && out_dtype != dtype) return PKV_ENOTSUP;
+  if (head_dim != 64 && head_dim != 128) return PKV_ENOTSUP;
+  if (num_heads <= 0 || num_heads > 65535 || num_prompts < 0 || num_prompts > 65535) return PKV_EINVAL;
+  if (total_tokens < 0 || max_prompt_len < 0) return PKV_EINVAL;
+  if (num_prompts == 0 || max_prompt_len == 0 || total_tokens == 0) return PKV_OK;
+  if (!q || !k || !v || !out || !prompt_lens) return PKV_EINVAL;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) || !aligned(prompt_lens, 4))
+    return PKV_EINVAL;
+  if (block_tables != nullptr &&
+      (max_blocks_per_seq <= 0 || (int64_t)max_blocks_per_seq * kBlock < (int64_t)max_prompt_len))
+    return PKV_EINVAL;
+  int st = device_status();
+  if (st != PKV_OK) return st;
+  hipStream_t sm = reinterpret_cast<hipStream_t>(stream);
+  if (validate_mode()) {
+    std::vector<int32_t> lens;
+    if (!copy_to_host(lens, prompt_lens, (size_t)num_prompts, sm)) return PKV_EDEVICE;
+    int64_t sum = 0;
+    for (int32_t x : lens) {
+      if (x < 0 || x > max_prompt_len) return PKV_EINVAL;
+      sum += x;
+    }
+    if (sum != total_tokens) return PKV_EINVAL;
+  }
+  pkv::PrefillArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.prompt_lens = prompt_lens;
+  a.out = out;
+  a.total_tokens = total_tokens;
+  a.num_prompts = num_prompts;
+  a.num_heads = num_heads;
+  a.max_prompt_len = max_prompt_len;
+  a.num_qtiles = (max_prompt_len + pkv::PREFILL_BLOCK_M - 1) / pkv::PREFILL_BLOCK_M;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  return launch_status(pkv::launch_prefill(a, dtype, out_dtype, head_dim, sm));
+}
+
+}  // extern "C"

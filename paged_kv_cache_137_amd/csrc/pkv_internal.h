@@ -1,0 +1,68 @@
+// Host-side interface between the C ABI (pkv_api.cpp) and the kernel launchers
+// in the .hip files.  Arguments here are already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkv {
+
+struct WriteArgs {
+  const void* k;
+  const void* v;
+  const int64_t* slot_mapping;
+  int64_t num_tokens;
+  void* k_cache;
+  void* v_cache;
+  int64_t num_blocks;
+  int32_t num_heads;
+  int32_t head_dim;
+  int32_t dtype;
+};
+
+// Arguments shared by the two decode stages.
+struct DecodeArgs {
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  void* out;
+  float* ws_acc;  // [S][H][P][D] unnormalised partial outputs
+  float* ws_ml;   // [S][H][P][2]  running max (log2 units) and sum
+  int64_t num_blocks;
+  int32_t num_heads;
+  int32_t max_blocks_per_seq;
+  int32_t num_seqs;
+  int32_t max_context_len;
+  int32_t part_blocks;  // blocks per partition
+  int32_t num_parts;    // P: partitions of the longest allowed context
+  int32_t per_xcd;      // workgroups per XCD slice of the grid
+  int32_t total_units;  // H * S * P
+  float scale_log2;     // scale * log2(e)
+};
+
+struct PrefillArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* prompt_lens;
+  void* out;
+  int64_t total_tokens;
+  int32_t num_prompts;
+  int32_t num_heads;
+  int32_t max_prompt_len;
+  int32_t num_qtiles;
+  float scale_log2;
+};
+
+// Each returns a hipError_t from the launch.
+hipError_t launch_kv_cache_write(const WriteArgs& a, hipStream_t stream);
+hipError_t launch_decode_partial(const DecodeArgs& a, int dtype, int out_dtype, int head_dim, hipStream_t stream);
+hipError_t launch_decode_reduce(const DecodeArgs& a, int out_dtype, int head_dim, hipStream_t stream);
+hipError_t launch_prefill(const PrefillArgs& a, int dtype, int out_dtype, int head_dim, hipStream_t stream);
+
+// Prefill query-tile height (rows per workgroup).
+constexpr int PREFILL_BLOCK_M = 128;
+
+}  // namespace pkv

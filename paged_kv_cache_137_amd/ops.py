@@ -1,0 +1,179 @@
+"""Python entry points of the paged-attention hot path, over torch device tensors.
+
+Each function checks shapes and dtypes, then hands raw device pointers, sizes and
+the current HIP stream to the matching C call in libpkv.so.  torch only provides
+memory and the stream.  The computation is entirely in the library's kernels.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+
+import torch
+
+from . import _lib
+from ._lib import CacheDesc, check, lib
+
+BLOCK_SIZE = 16
+DEFAULT_PARTITION = 512
+
+_DT = {torch.float32: _lib.PKV_F32, torch.float16: _lib.PKV_F16, torch.bfloat16: _lib.PKV_BF16}
+
+
+def pkv_dtype(dt: torch.dtype) -> int:
+    try:
+        return _DT[dt]
+    except KeyError:
+        raise ValueError(f"unsupported dtype {dt}; use float32, float16 or bfloat16") from None
+
+
+def _ptr(t: torch.Tensor | None) -> ctypes.c_void_p:
+    return ctypes.c_void_p(0 if t is None else t.data_ptr())
+
+
+def _stream(dev: torch.device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, dtype=None, dim=None, device=None) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if dim is not None and t.dim() != dim:
+        raise ValueError(f"{name} must have {dim} dims, got {tuple(t.shape)}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def cache_desc(k_cache: torch.Tensor) -> CacheDesc:
+    nb, H, B, D = k_cache.shape
+    return CacheDesc(nb, H, D, B, pkv_dtype(k_cache.dtype))
+
+
+def kv_cache_write(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor,
+                   k_cache: torch.Tensor, v_cache: torch.Tensor) -> None:
+    """Write new tokens' K/V [T][H][D] into the slots slot_mapping (int64 [T]) names."""
+    _need(k_cache, "k_cache", dim=4)
+    dev = k_cache.device
+    _need(v_cache, "v_cache", dtype=k_cache.dtype, device=dev)
+    _need(k, "k", dtype=k_cache.dtype, dim=3, device=dev)
+    _need(v, "v", dtype=k_cache.dtype, dim=3, device=dev)
+    _need(slot_mapping, "slot_mapping", dtype=torch.int64, dim=1, device=dev)
+    if v_cache.shape != k_cache.shape or v.shape != k.shape:
+        raise ValueError("k/v and k_cache/v_cache shapes must match")
+    T, H, D = k.shape
+    if (H, D) != (k_cache.shape[1], k_cache.shape[3]) or slot_mapping.shape[0] != T:
+        raise ValueError("k [T][H][D] does not match the cache or slot_mapping")
+    desc = cache_desc(k_cache)
+    with torch.cuda.device(dev):
+        check("pkv_kv_cache_write", lib().pkv_kv_cache_write(
+            _ptr(k), _ptr(v), _ptr(slot_mapping), T, _ptr(k_cache), _ptr(v_cache), ctypes.byref(desc), _stream(dev)))
+
+
+def decode_workspace_bytes(num_seqs: int, num_heads: int, head_dim: int, max_context_len: int,
+                           partition_size: int = DEFAULT_PARTITION) -> int:
+    return int(lib().pkv_decode_workspace_bytes(num_seqs, num_heads, head_dim, max_context_len, partition_size))
+
+
+def _decode_call(fn_name, q, k_cache, v_cache, block_tables, context_lens, scale, out,
+                 max_context_len, partition_size, workspace):
+    _need(k_cache, "k_cache", dim=4)
+    dev = k_cache.device
+    _need(v_cache, "v_cache", dtype=k_cache.dtype, device=dev)
+    _need(q, "q", dtype=k_cache.dtype, dim=3, device=dev)
+    _need(block_tables, "block_tables", dtype=torch.int32, dim=2, device=dev)
+    _need(context_lens, "context_lens", dtype=torch.int32, dim=1, device=dev)
+    _need(out, "out", dim=3, device=dev)
+    S, H, D = q.shape
+    if v_cache.shape != k_cache.shape or (H, D) != (k_cache.shape[1], k_cache.shape[3]):
+        raise ValueError("q [S][H][D] does not match the cache")
+    if out.shape != q.shape or out.dtype not in (torch.float32, q.dtype):
+        raise ValueError("out must be [S][H][D] of float32 or q's dtype")
+    if block_tables.shape[0] != S or context_lens.shape[0] != S:
+        raise ValueError("block_tables/context_lens must have one row per sequence")
+    mbps = block_tables.shape[1]
+    if max_context_len is None:
+        max_context_len = mbps * k_cache.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    need = decode_workspace_bytes(S, H, D, max_context_len, partition_size) if S else 0
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    if workspace is not None:
+        _need(workspace, "workspace", device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    desc = cache_desc(k_cache)
+    with torch.cuda.device(dev):
+        check(fn_name, getattr(lib(), fn_name)(
+            _ptr(q), _ptr(k_cache), _ptr(v_cache), ctypes.byref(desc), _ptr(block_tables), mbps,
+            _ptr(context_lens), S, int(max_context_len), float(scale), _ptr(out), pkv_dtype(out.dtype),
+            int(partition_size), _ptr(workspace), ws_bytes, _stream(dev)))
+    return out
+
+
+def paged_attn_decode(q, k_cache, v_cache, block_tables, context_lens, scale, out, *,
+                      max_context_len: int | None = None, partition_size: int = DEFAULT_PARTITION,
+                      workspace: torch.Tensor | None = None):
+    """Decode attention of q [S][H][D] over each sequence's paged context; fills out.
+
+    max_context_len bounds every context_lens entry.  By default it is the table
+    capacity (max_blocks_per_seq * block_size).  partition_size = 0 disables the
+    split-context path.  Without a workspace, one is allocated through torch.
+    """
+    return _decode_call("pkv_paged_attn_decode", q, k_cache, v_cache, block_tables, context_lens, scale, out,
+                        max_context_len, partition_size, workspace)
+
+
+def paged_attn_decode_partial(q, k_cache, v_cache, block_tables, context_lens, scale, out, *,
+                              max_context_len=None, partition_size=DEFAULT_PARTITION, workspace=None):
+    """First stage of paged_attn_decode (per-partition kernel only)."""
+    return _decode_call("pkv_paged_attn_decode_partial", q, k_cache, v_cache, block_tables, context_lens, scale,
+                        out, max_context_len, partition_size, workspace)
+
+
+def paged_attn_decode_reduce(q, k_cache, v_cache, block_tables, context_lens, scale, out, *,
+                             max_context_len=None, partition_size=DEFAULT_PARTITION, workspace=None):
+    """Second stage of paged_attn_decode (split-context reduce only)."""
+    return _decode_call("pkv_paged_attn_decode_reduce", q, k_cache, v_cache, block_tables, context_lens, scale,
+                        out, max_context_len, partition_size, workspace)
+
+
+def paged_attn_prefill(q, k, v, block_tables, prompt_lens, out, *, scale: float | None = None,
+                       max_prompt_len: int | None = None):
+    """Causal attention of packed prompts q/k/v [T][H][D] (f16 or bf16); fills out.
+
+    prompt_lens is an int32 device tensor.  max_prompt_len bounds its entries;
+    by default it is T.  block_tables may be None.  It is reserved, because the
+    prompt's contiguous k/v hold the same bytes as its blocks once written.
+    """
+    _need(q, "q", dim=3)
+    dev = q.device
+    _need(k, "k", dtype=q.dtype, device=dev)
+    _need(v, "v", dtype=q.dtype, device=dev)
+    _need(prompt_lens, "prompt_lens", dtype=torch.int32, dim=1, device=dev)
+    _need(out, "out", dim=3, device=dev)
+    if k.shape != q.shape or v.shape != q.shape or out.shape != q.shape:
+        raise ValueError("q, k, v and out must all be [T][H][D]")
+    if out.dtype not in (torch.float32, q.dtype):
+        raise ValueError("out must be float32 or q's dtype")
+    T, H, D = q.shape
+    mbps = 0
+    if block_tables is not None:
+        _need(block_tables, "block_tables", dtype=torch.int32, dim=2, device=dev)
+        mbps = block_tables.shape[1]
+    if max_prompt_len is None:
+        max_prompt_len = T
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    with torch.cuda.device(dev):
+        check("pkv_paged_attn_prefill", lib().pkv_paged_attn_prefill(
+            _ptr(q), _ptr(k), _ptr(v), H, D, pkv_dtype(q.dtype), _ptr(block_tables), mbps, _ptr(prompt_lens),
+            prompt_lens.shape[0], T, int(max_prompt_len), float(scale), _ptr(out), pkv_dtype(out.dtype),
+            _stream(dev)))
+    return out

@@ -1,0 +1,114 @@
+"""The C-ABI library loads here (no GPU) and exports every symbol include/pkv.h declares.
+
+Only calls that need no device are made: version, status strings, workspace
+sizing and argument rejection that happens before any device query.
+"""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from paged_kv_cache_137_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pkv.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pkv_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        from paged_kv_cache_137_amd.build import build_library
+
+        build_library()
+    return _lib.lib()
+
+
+def test_header_declares_the_boundary():
+    names = _declared()
+    for n in ("pkv_kv_cache_write", "pkv_paged_attn_decode", "pkv_paged_attn_prefill"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True, check=True)
+    exported = set(re.findall(r"\bT (pkv_\w+)", out.stdout))
+    missing = [n for n in _declared() if n not in exported]
+    assert not missing, missing
+    for n in _declared():
+        assert getattr(lib, n) is not None
+    assert set(_lib.SIGNATURES) == set(_declared())
+
+
+def test_version_and_status_strings(lib):
+    assert lib.pkv_abi_version() == 1
+    assert lib.pkv_status_str(0) == b"ok"
+    assert b"invalid" in lib.pkv_status_str(_lib.PKV_EINVAL)
+    assert lib.pkv_status_str(12345) == b"unknown status"
+
+
+def test_workspace_sizing(lib):
+    # 256 seqs x 32 heads x ceil(4096/512)=8 partitions x (128 + 2) floats
+    assert lib.pkv_decode_workspace_bytes(256, 32, 128, 4096, 512) == 256 * 32 * 8 * 130 * 4
+    assert lib.pkv_decode_workspace_bytes(256, 32, 128, 512, 512) == 0  # one partition: no split
+    assert lib.pkv_decode_workspace_bytes(256, 32, 128, 4096, 0) == 0   # split disabled
+    assert lib.pkv_decode_workspace_bytes(0, 32, 128, 4096, 512) == 0
+
+
+def test_bad_arguments_rejected_before_any_launch(lib):
+    desc = _lib.CacheDesc(64, 4, 128, 16, _lib.PKV_BF16)
+    null = ctypes.c_void_p(0)
+    # NULL descriptor
+    assert lib.pkv_kv_cache_write(null, null, null, 1, null, null, None, null) == _lib.PKV_EINVAL
+    # unsupported block size / head dim
+    bad_b = _lib.CacheDesc(64, 4, 128, 8, _lib.PKV_BF16)
+    assert lib.pkv_kv_cache_write(null, null, null, 1, null, null, ctypes.byref(bad_b), null) == _lib.PKV_ENOTSUP
+    bad_d = _lib.CacheDesc(64, 4, 96, 16, _lib.PKV_BF16)
+    assert lib.pkv_kv_cache_write(null, null, null, 1, null, null, ctypes.byref(bad_d), null) == _lib.PKV_ENOTSUP
+    # NULL data pointers
+    assert lib.pkv_kv_cache_write(null, null, null, 1, null, null, ctypes.byref(desc), null) == _lib.PKV_EINVAL
+    # zero tokens is a no-op
+    assert lib.pkv_kv_cache_write(null, null, null, 0, null, null, ctypes.byref(desc), null) == _lib.PKV_OK
+    # decode: context longer than the table can hold
+    rc = lib.pkv_paged_attn_decode(null, null, null, ctypes.byref(desc), null, 4, null, 1, 65, 1.0, null, 0, 512,
+                                   null, 0, null)
+    assert rc == _lib.PKV_EINVAL
+    # decode: bad partition size, bad output dtype
+    rc = lib.pkv_paged_attn_decode(null, null, null, ctypes.byref(desc), null, 4, null, 1, 64, 1.0, null, 0, 100,
+                                   null, 0, null)
+    assert rc == _lib.PKV_EINVAL
+    rc = lib.pkv_paged_attn_decode(null, null, null, ctypes.byref(desc), null, 4, null, 1, 64, 1.0, null,
+                                   _lib.PKV_F16, 512, null, 0, null)
+    assert rc == _lib.PKV_ENOTSUP
+    # decode: empty batch is a no-op
+    rc = lib.pkv_paged_attn_decode(null, null, null, ctypes.byref(desc), null, 4, null, 0, 64, 1.0, null, 0, 512,
+                                   null, 0, null)
+    assert rc == _lib.PKV_OK
+    # prefill: fp32 inputs are not built; head_dim 96 is not built
+    rc = lib.pkv_paged_attn_prefill(null, null, null, 4, 128, _lib.PKV_F32, null, 0, null, 1, 10, 10, 1.0, null, 0,
+                                    null)
+    assert rc == _lib.PKV_ENOTSUP
+    rc = lib.pkv_paged_attn_prefill(null, null, null, 4, 96, _lib.PKV_BF16, null, 0, null, 1, 10, 10, 1.0, null, 0,
+                                    null)
+    assert rc == _lib.PKV_ENOTSUP
+    # prefill: nothing to do
+    rc = lib.pkv_paged_attn_prefill(null, null, null, 4, 128, _lib.PKV_BF16, null, 0, null, 0, 0, 0, 1.0, null, 0,
+                                    null)
+    assert rc == _lib.PKV_OK
+
+
+def test_python_package_imports_without_gpu():
+    import paged_kv_cache_137_amd as pkg
+
+    assert pkg.BlockManager is not None
+    from paged_kv_cache_137_amd import ops
+
+    assert ops.pkv_dtype.__name__ == "pkv_dtype"

@@ -1,0 +1,107 @@
+"""Causal prefill on the GPU (MFMA) against the float64 oracle; the mixed step of config 5."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from paged_kv_cache_137_amd import ops
+from paged_kv_cache_137_amd import workloads as W
+from paged_kv_cache_137_amd.blocks import slot_mapping
+from _dev import TOL, TORCH_DT, bits, down, rne_to, run_decode, sample_seqs, up, upload_decode
+
+pytestmark = pytest.mark.gpu
+
+
+def _prefill(p, out_dtype="f32", heads=None):
+    q, k, v = p.q, p.k, p.v
+    if heads is not None:
+        q, k, v = (np.ascontiguousarray(x[:, heads]) for x in (q, k, v))
+    out = torch.empty(q.shape, dtype=TORCH_DT[out_dtype], device="cuda")
+    ops.paged_attn_prefill(up(q, p.dtype), up(k, p.dtype), up(v, p.dtype), None, up(p.prompt_lens), out,
+                           max_prompt_len=int(p.prompt_lens.max()))
+    return out
+
+
+@pytest.mark.parametrize("dt,D", [("bf16", 128), ("f16", 128), ("bf16", 64), ("f16", 64)])
+def test_prefill_parity_ragged(dt, D):
+    lens = [1, 2, 17, 63, 64, 65, 127, 128, 129, 300, 0, 513]
+    print(f"prefill parity {dt} D={D}", flush=True)
+    p = W.make_prefill(71, dt, 4, D, lens)
+    out32 = down(_prefill(p))
+    ref = oracle.attention.causal_prefill(p.q, p.k, p.v, p.prompt_lens, 1 / math.sqrt(D), dt)
+    assert np.isfinite(out32).all()
+    err = float(np.abs(out32 - ref).max())
+    print(f"  max|err|={err:.3e}", flush=True)
+    assert err <= TOL[dt]
+    outdt = down(_prefill(p, dt))
+    assert np.array_equal(bits(outdt), bits(rne_to(out32, dt)))
+    # row 0 of every prompt is v_0 exactly
+    offs = np.concatenate([[0], np.cumsum(lens)])[:-1]
+    for o, L in zip(offs, lens):
+        if L:
+            assert np.array_equal(out32[o].astype(np.float64), oracle.attention.to_f64(p.v[o], dt))
+
+
+def test_prefill_last_row_matches_decode():
+    print("prefill <-> decode consistency", flush=True)
+    dt, H, D, L = "bf16", 4, 128, 777
+    p = W.make_prefill(72, dt, H, D, [L])
+    out_p = down(_prefill(p))
+    nb = -(-L // 16)
+    kc = np.zeros((nb + 1, H, 16, D), np.uint16); vc = np.zeros_like(kc)
+    table = np.random.default_rng(0).permutation(nb + 1).astype(np.int32)
+    for t_ in range(L):
+        kc[table[t_ // 16], :, t_ % 16] = p.k[t_]
+        vc[table[t_ // 16], :, t_ % 16] = p.v[t_]
+    d = W.DecodeInputs(name="consistency", dtype=dt, num_heads=H, head_dim=D, block_size=16, num_blocks=nb + 1,
+                       scale=1 / math.sqrt(D), context_lens=np.array([L], np.int32), block_tables=table[None, :],
+                       k_cache=kc, v_cache=vc, q=p.q[L - 1 : L].copy(), pad_block=int(table[nb]))
+    out_d = down(run_decode(ops, upload_decode(d), d, "f32"))
+    assert np.abs(out_p[L - 1] - out_d[0]).max() <= TOL[dt]
+
+
+def test_mixed_step_config5():
+    """Config 5 at full size: write (8 prompts + 192 decode tokens) -> prefill -> decode + reduce."""
+    print("mixed step config 5", flush=True)
+    mx = W.mixed_config()
+    d, p = mx.decode, mx.prefill
+    B = 16
+    # host bookkeeping: the prompts' slots, then the decode tokens' slots
+    seq_p = np.repeat(np.arange(len(p.prompt_lens)), p.prompt_lens)
+    pos_p = np.concatenate([np.arange(L) for L in p.prompt_lens])
+    sm = np.concatenate([slot_mapping(p.block_tables, seq_p, pos_p, B),
+                         slot_mapping(d.block_tables, np.arange(d.num_seqs), d.context_lens - 1, B)])
+    sm_ref = np.concatenate([oracle.bookkeeping.slot_mapping(p.block_tables, seq_p, pos_p, B),
+                             oracle.bookkeeping.slot_mapping(d.block_tables, range(d.num_seqs), d.context_lens - 1, B)])
+    assert np.array_equal(sm, sm_ref)
+    k_all = np.concatenate([p.k, d.k_new]); v_all = np.concatenate([p.v, d.v_new])
+
+    t = upload_decode(d)
+    ops.kv_cache_write(up(k_all, d.dtype), up(v_all, d.dtype), up(sm), t["k_cache"], t["v_cache"])
+    pout = torch.empty(p.q.shape, dtype=torch.float32, device="cuda")
+    ops.paged_attn_prefill(up(p.q, p.dtype), up(p.k, p.dtype), up(p.v, p.dtype), up(p.block_tables),
+                           up(p.prompt_lens), pout, max_prompt_len=int(p.prompt_lens.max()))
+    dout = run_decode(ops, t, d, "f32")
+    torch.cuda.synchronize()
+
+    ek, ev = oracle.attention.cache_write(d.k_cache, d.v_cache, k_all, v_all, sm, B)
+    assert np.array_equal(bits(down(t["k_cache"])), bits(ek))
+    assert np.array_equal(bits(down(t["v_cache"])), bits(ev))
+    del t
+
+    seqs = sample_seqs(d.context_lens, 32)
+    ref = oracle.attention.paged_decode(d.q, ek, ev, d.block_tables, d.context_lens, d.scale, d.dtype, seqs=seqs)
+    got = down(dout)
+    assert np.isfinite(got).all()
+    derr = float(np.abs(got[seqs] - ref[seqs]).max())
+    heads = [0, 13, 31]
+    pref = oracle.attention.causal_prefill(*(np.ascontiguousarray(x[:, heads]) for x in (p.q, p.k, p.v)),
+                                           p.prompt_lens, 1 / math.sqrt(p.head_dim), p.dtype)
+    pgot = down(pout)
+    assert np.isfinite(pgot).all()
+    perr = float(np.abs(pgot[:, heads] - pref).max())
+    print(f"  decode max|err|={derr:.3e}  prefill max|err|={perr:.3e}", flush=True)
+    assert derr <= TOL[d.dtype] and perr <= TOL[p.dtype]
