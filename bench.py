@@ -1,0 +1,314 @@
+"""Benchmark of the paged-attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+A step is one decode step of the Llama-2-7B-shaped workload: 256 sequences,
+32 heads x 128, bf16, 16-token blocks, context lengths lognormal (median 600,
+sigma 0.8) clipped to [16, 4096], in shuffled physical blocks.  The step
+  1. writes the 256 current tokens' K/V into their slots (kv_cache_write),
+  2. runs the per-partition decode kernel (512-token partitions),
+  3. runs the split-context reduce.
+Inputs are resident in HBM before the timed region starts.  One JSON line is
+printed.  value = KV bytes attended per step (sum of context lengths x 2 x heads
+x head_dim x 2 B) / wall time per step.
+
+The same line also carries:
+  roofline      the decode kernel alone.  Algorithmic bytes per launch / its
+                mean duration from HIP events on the launch stream, against
+                MI355X's 8 TB/s.  traffic comes from the committed rocprofv3
+                counter summary, if it was taken on this kernel source.
+  cpu_baseline  the float64 CPU oracle, one thread, on a time-boxed sample of
+                the same step's sequences.
+  mixed_step    the mixed prefill+decode step (8 prompts prefilled while 192
+                sequences decode), per kernel, with prefill's MFMA rate.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "paged decode attention: KV HBM GB/s (% of peak) + tokens attended/s"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "paged_decode_pmc.txt")
+DECODE_SOURCE = os.path.join(ROOT, "paged_kv_cache_137_amd", "csrc", "paged_decode.hip")
+
+
+def _args():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--partition", type=int, default=512)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-mixed", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="time box of the CPU oracle sample")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain device copy of a known size (for counter calibration) and exit")
+    return ap.parse_args()
+
+
+def source_digest(path: str = DECODE_SOURCE) -> str:
+    with open(path, "rb") as f:
+        return hashlib.sha1(f.read()).hexdigest()[:12]
+
+
+def read_pmc_summary():
+    """Counter-derived HBM bytes per decode launch, if taken on the current kernel source."""
+    if not os.path.exists(PMC_SUMMARY):
+        return None
+    kv = {}
+    for line in open(PMC_SUMMARY):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    try:
+        if kv.get("decode_source_sha1") != source_digest():
+            return None
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def main() -> int:
+    a = _args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if a.gpus != 1 or world != 1:
+        print("bench.py measures one MI355X: this build has no multi-GPU path "
+              "(--gpus must be 1).", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    from paged_kv_cache_137_amd import ops
+    from paged_kv_cache_137_amd import workloads as W
+    from paged_kv_cache_137_amd.blocks import slot_mapping
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def up(x, dt=None):
+        x = np.ascontiguousarray(x)
+        if dt == "bf16":
+            return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(x).to(dev)
+
+    if a.copy_calibration:
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n}))
+        return 0
+
+    # ---------------- decode step (the headline) ----------------
+    d = W.decode_config(3, poison=False, with_new_tokens=True)
+    S, H, D = d.q.shape
+    sum_ctx = int(d.context_lens.sum())
+    kv_bytes = sum_ctx * 2 * H * D * 2
+    t = dict(q=up(d.q, "bf16"), kc=up(d.k_cache, "bf16"), vc=up(d.v_cache, "bf16"),
+             bt=up(d.block_tables), cl=up(d.context_lens), kn=up(d.k_new, "bf16"), vn=up(d.v_new, "bf16"))
+    t["sm"] = up(slot_mapping(d.block_tables, np.arange(S), d.context_lens - 1))
+    out = torch.empty((S, H, D), dtype=torch.bfloat16, device=dev)
+    mcl = d.max_context_len
+    ws = torch.empty(max(1, ops.decode_workspace_bytes(S, H, D, mcl, a.partition)), dtype=torch.uint8, device=dev)
+    dargs = (t["q"], t["kc"], t["vc"], t["bt"], t["cl"], d.scale, out)
+    dkw = dict(max_context_len=mcl, partition_size=a.partition, workspace=ws)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        ops.kv_cache_write(t["kn"], t["vn"], t["sm"], t["kc"], t["vc"])
+        if ev is not None:
+            ev[1].record()
+        ops.paged_attn_decode_partial(*dargs, **dkw)
+        if ev is not None:
+            ev[2].record()
+        ops.paged_attn_decode_reduce(*dargs, **dkw)
+        if ev is not None:
+            ev[3].record()
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(a.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / a.steps
+
+    # per-kernel durations from HIP events on the launch stream (a separate, equal pass)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(a.steps)]
+    for e in evs:
+        step(e)
+    torch.cuda.synchronize()
+    k_write = sum(e[0].elapsed_time(e[1]) for e in evs) / a.steps
+    k_dec = sum(e[1].elapsed_time(e[2]) for e in evs) / a.steps
+    k_red = sum(e[2].elapsed_time(e[3]) for e in evs) / a.steps
+
+    value = kv_bytes / (ms_step * 1e-3) / 1e9
+    achieved = kv_bytes / (k_dec * 1e-3) / 1e9
+    traffic = read_pmc_summary()
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "Llama-2-7B-shape paged decode step: 256 seqs, 32 heads x 128, bf16, 16-token blocks, "
+                        "ctx lognormal(600, 0.8) in [16, 4096], shuffled blocks, 512-token partitions + reduce",
+            "num_seqs": S, "num_heads": H, "head_dim": D, "block_size": 16, "partition_size": a.partition,
+            "sum_context_len": sum_ctx, "max_context_len": mcl, "num_blocks": d.num_blocks,
+            "seed": W.config_seed(3),
+        },
+        "pct_of_peak_hbm": round(100 * value / HBM_PEAK_GBS, 2),
+        "tokens_attended_per_s": round(sum_ctx / (ms_step * 1e-3), 1),
+        "head_tokens_attended_per_s": round(sum_ctx * H / (ms_step * 1e-3), 1),
+        "kernels_ms": {"kv_cache_write": round(k_write, 5), "paged_decode_partial": round(k_dec, 5),
+                       "paged_decode_reduce": round(k_red, 5)},
+        "roofline": {
+            "bound": "hbm", "kernel": "decode_partial_kernel<bf16,bf16,128>",
+            "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "algorithmic_bytes": kv_bytes,
+            "traffic": None if traffic is None else int(traffic),
+        },
+    }
+    del t, ws, out
+    torch.cuda.empty_cache()
+
+    # ---------------- mixed prefill + decode step ----------------
+    if not a.no_mixed:
+        line["mixed_step"] = mixed_step(a, dev, up)
+
+    # ---------------- CPU oracle baseline ----------------
+    if not a.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(d, a.cpu_seconds)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def mixed_step(a, dev, up):
+    import numpy as np
+    import torch
+
+    from paged_kv_cache_137_amd import ops
+    from paged_kv_cache_137_amd import workloads as W
+    from paged_kv_cache_137_amd.blocks import slot_mapping
+
+    mx = W.mixed_config(poison=False)
+    d, p = mx.decode, mx.prefill
+    S, H, D = d.q.shape
+    seq_p = np.repeat(np.arange(len(p.prompt_lens)), p.prompt_lens)
+    pos_p = np.concatenate([np.arange(L) for L in p.prompt_lens])
+    sm = np.concatenate([slot_mapping(p.block_tables, seq_p, pos_p),
+                         slot_mapping(d.block_tables, np.arange(S), d.context_lens - 1)])
+    k_all = up(np.concatenate([p.k, d.k_new]), "bf16")
+    v_all = up(np.concatenate([p.v, d.v_new]), "bf16")
+    kc, vc = up(d.k_cache, "bf16"), up(d.v_cache, "bf16")
+    pq, pk, pv = up(p.q, "bf16"), up(p.k, "bf16"), up(p.v, "bf16")
+    plens, ptab = up(p.prompt_lens), up(p.block_tables)
+    q, bt, cl, smd = up(d.q, "bf16"), up(d.block_tables), up(d.context_lens), up(sm)
+    pout = torch.empty(pq.shape, dtype=torch.bfloat16, device=dev)
+    dout = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
+    mpl, mcl = int(p.prompt_lens.max()), d.max_context_len
+    ws = torch.empty(max(1, ops.decode_workspace_bytes(S, H, D, mcl, 512)), dtype=torch.uint8, device=dev)
+
+    def run(ev=None):
+        if ev is not None:
+            ev[0].record()
+        ops.kv_cache_write(k_all, v_all, smd, kc, vc)
+        if ev is not None:
+            ev[1].record()
+        ops.paged_attn_prefill(pq, pk, pv, ptab, plens, pout, max_prompt_len=mpl)
+        if ev is not None:
+            ev[2].record()
+        ops.paged_attn_decode(q, kc, vc, bt, cl, d.scale, dout, max_context_len=mcl, partition_size=512,
+                              workspace=ws)
+        if ev is not None:
+            ev[3].record()
+
+    for _ in range(a.warmup):
+        run()
+    n = max(5, a.steps // 2)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e in evs:
+        run(e)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / n
+    w_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / n
+    p_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / n
+    d_ms = sum(e[2].elapsed_time(e[3]) for e in evs) / n
+    T = int(k_all.shape[0])
+    write_bytes = 2 * T * H * D * 2 * 2
+    L = p.prompt_lens.astype(np.int64)
+    flops = 4.0 * D * H * float((L * (L + 1) // 2).sum())
+    dec_bytes = int(d.context_lens.sum()) * 2 * H * D * 2
+    return {
+        "workload": "8 prompts U[128,2048] prefilled into fresh shuffled blocks + 192 decodes lognormal(800,0.8), "
+                    "32 heads x 128, bf16",
+        "ms_per_step": round(wall_ms, 4),
+        "kernels_ms": {"kv_cache_write": round(w_ms, 5), "paged_attn_prefill": round(p_ms, 5),
+                       "paged_attn_decode": round(d_ms, 5)},
+        "write_GBps": round(write_bytes / (w_ms * 1e-3) / 1e9, 1),
+        "prefill_tokens": int(L.sum()),
+        "prefill_TFLOPs": round(flops / (p_ms * 1e-3) / 1e12, 1),
+        "prefill_mfma_frac": round(flops / (p_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+        "decode_GBps": round(dec_bytes / (d_ms * 1e-3) / 1e9, 1),
+        "decode_tokens_attended_per_s": round(float(d.context_lens.sum()) / (d_ms * 1e-3), 1),
+    }
+
+
+def cpu_baseline(d, seconds: float):
+    """The float64 oracle on whole sequences of the same step, one thread, until `seconds` pass."""
+    import numpy as np
+    import threadpoolctl
+
+    import oracle
+
+    H, D = d.num_heads, d.head_dim
+    done, tokens = 0, 0
+    with threadpoolctl.threadpool_limits(1):
+        t0 = time.perf_counter()
+        while done < d.num_seqs and (time.perf_counter() - t0) < seconds:
+            oracle.attention.paged_decode(d.q, d.k_cache, d.v_cache, d.block_tables, d.context_lens, d.scale,
+                                          d.dtype, seqs=[done])
+            tokens += int(d.context_lens[done])
+            done += 1
+        el = time.perf_counter() - t0
+    return {
+        "value": round(tokens * 2 * H * D * 2 / el / 1e9, 4),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "tokens_attended_per_s": round(tokens / el, 1),
+        "sample": f"first {done} of {d.num_seqs} sequences of the same decode step ({tokens} tokens, "
+                  f"{el:.1f} s), float64 NumPy, BLAS limited to 1 thread",
+    }
+
+
+if __name__ == "__main__":
+    sys.exit(main())

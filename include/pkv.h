@@ -112,10 +112,14 @@ int pkv_kv_cache_write(const void* k, const void* v, const int64_t* slot_mapping
                        void* k_cache, void* v_cache, const pkv_cache_desc* desc, void* stream);
 
 /*
- * Workspace for pkv_paged_attn_decode: partial results of the split-context
- * decode, in float32.  num_seqs * num_heads * P * (head_dim + 2) * 4 bytes,
- * where P = ceil(max_context_len / partition_size).  The size is 0 when
- * partition_size == 0 (no split) or no sequence can span two partitions.
+ * Workspace for pkv_paged_attn_decode, in bytes.  P = ceil(max_context_len /
+ * partition_size), or 1 when partition_size == 0.  The workspace holds:
+ *   - a work counter (16 B);
+ *   - the list of (sequence, partition) units (num_seqs * P int32);
+ *   - when P > 1, the partial results of the split-context decode in float32
+ *     (num_seqs * num_heads * P * (head_dim + 2) * 4 B).
+ * Its contents need no initialisation.  Each call rebuilds what it uses.
+ * Returns 0 only for an empty or invalid shape.
  */
 size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
                                   int32_t max_context_len, int32_t partition_size);
@@ -146,12 +150,14 @@ size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t h
  *                 is one workgroup.  A sequence spanning more than one partition
  *                 is merged by a second, reduce kernel (max-rescaled sum of the
  *                 partial results), in a fixed order.
- *   workspace     device scratch of at least pkv_decode_workspace_bytes(...)
- *                 (may be NULL when that is 0).  The caller owns it.  Calls that
- *                 run at the same time need separate workspaces.
- * Results are deterministic: no atomics, and the merge order is fixed.  The
- * output does not depend on which physical ids hold the blocks, or on whether
- * blocks are shared.  A table entry outside [0, num_blocks) makes that
+ *   workspace     device scratch of at least pkv_decode_workspace_bytes(...),
+ *                 owned by the caller.  Calls that can run at the same time
+ *                 (different streams) need separate workspaces.
+ * Work is spread by a small plan kernel and a persistent kernel that claims
+ * units from a counter in the workspace.  No arithmetic depends on that order,
+ * and the merge order of partitions is fixed, so results are deterministic,
+ * bit for bit.  The output does not depend on which physical ids hold the
+ * blocks, or on whether blocks are shared.  A table entry outside [0, num_blocks) makes that
  * sequence's output NaN instead of reading out of bounds.
  */
 int pkv_paged_attn_decode(const void* q, const void* k_cache, const void* v_cache, const pkv_cache_desc* desc,

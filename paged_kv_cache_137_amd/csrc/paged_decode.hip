@@ -5,39 +5,62 @@
 // sequence ("vLLM & PagedAttention: Efficient Memory Management for LLM
 // Serving", section I, attention equation).  It is evaluated block by block
 // (section III, block-wise equation), with the normaliser carried across blocks
-// ("PagedAttention and vLLM, annotated", section 4.1: "normalize by the total
-// over all blocks so far").
+// ("PagedAttention and vLLM, annotated", section 4.1: normalise by the total over
+// all blocks so far).
 //
 // Work decomposition (designed for CDNA4, not taken from the pages):
-//  - One workgroup of 4 wavefronts per (sequence, head, context partition).
-//    Wave w takes the partition's blocks w, w+4, w+8, ... so a short last
-//    partition still spreads over all waves.
+//  - A unit of work is one (sequence, head, context partition).  A plan kernel
+//    (one workgroup) lists the (sequence, partition) pairs that hold tokens.
+//    It sorts them by size, largest first, with a counting sort, and resets a
+//    work counter.  The decode kernel is persistent.  Just enough 4-wave
+//    workgroups to fill the GPU claim units from the counter until none are
+//    left.  Empty partitions cost nothing, and the ragged tail is spread over
+//    the whole GPU.  No output depends on which workgroup ran which unit, so
+//    results are deterministic.
+//  - Inside a unit, wave w takes the partition's blocks w, w+4, w+8, ..., so a
+//    short partition still spreads over all waves.
 //  - A (block, head) tile is 16 tokens x D values stored contiguously.  A wave
 //    reads it with NI 16-byte loads per lane, each load instruction covering
 //    1 KiB of consecutive bytes.  Lane l holds dims (l % LPT)*VEC .. +VEC of
-//    token row l / LPT.
+//    token row l / LPT.  K/V are read with the nontemporal hint: every tile is
+//    used once per unit, and keeping it out of the cache hierarchy's
+//    retention raises the sustained HBM rate.
 //  - q.k: packed dot products (v_dot2 for 16-bit inputs) over the lane's VEC
 //    dims, then a DPP butterfly across the LPT lanes of the token row.  Every
 //    lane of the row ends with the same score.
 //  - Online softmax per token row: each lane row keeps its own running max,
 //    sum and VEC accumulators, so the steady state needs no cross-row traffic.
-//    Rows and waves are merged once, through LDS, at the end of the partition.
+//    Rows and waves are merged once per unit, through LDS.
 //  - Software pipelining: the next block's K/V loads are issued before the
 //    current block is consumed (ping-pong register sets, no branch between
 //    them), so two tiles per wave are in flight.
 //  - Masking of slots at or past the context length is a select (-inf score,
 //    zeroed V), never a multiply, so stale NaN data in those slots cannot leak.
-//  - Grid order: unit u = p + P*(s + S*h).  The hardware workgroup id is
-//    remapped so that each XCD walks a contiguous range of units.  The
-//    partitions of one sequence, and neighbouring sequences that share blocks,
-//    then run on the same XCD and hit its L2.
 #include "pkv_device.h"
 #include "pkv_internal.h"
 
 namespace pkv {
 
-constexpr int BS = 16;  // tokens per block
-constexpr int NW = 4;   // wavefronts per workgroup
+#ifndef PKV_DEC_NW
+#define PKV_DEC_NW 4
+#endif
+#ifndef PKV_DEC_NT
+#define PKV_DEC_NT 1
+#endif
+
+constexpr int BS = 16;             // tokens per block
+constexpr int NW = PKV_DEC_NW;     // wavefronts per workgroup
+constexpr int PLAN_BUCKETS = 257;  // partition sizes 0..256 blocks (larger ones share the top bucket)
+
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint4 load_kv16(const char* p) {
+#if PKV_DEC_NT
+  return __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p)));
+#else
+  return *reinterpret_cast<const uint4*>(p);
+#endif
+}
 
 template <typename E, int D>
 struct DecodeGeom {
@@ -50,6 +73,53 @@ struct DecodeGeom {
   static_assert(TPI * LPT == 64 && NI * TPI == BS, "tile must map onto a wavefront");
 };
 
+__device__ __forceinline__ int clamp_ctx(const DecodeArgs& a, int s) { return min(a.context_lens[s], a.max_context_len); }
+
+// List every (sequence, partition) that holds tokens, largest partitions first,
+// and reset the work counter.  A sequence with context_len <= 0 gets one entry
+// (partition 0, in the smallest bucket) so that its output is written as NaN.
+__global__ __launch_bounds__(1024) void decode_plan_kernel(const DecodeArgs a) {
+  __shared__ int cnt[PLAN_BUCKETS];
+  const int part_tokens = a.part_blocks * BS;
+  for (int i = threadIdx.x; i < PLAN_BUCKETS; i += blockDim.x) cnt[i] = 0;
+  __syncthreads();
+  for (int s = threadIdx.x; s < a.num_seqs; s += blockDim.x) {
+    const int ctx = clamp_ctx(a, s);
+    if (ctx <= 0) {
+      atomicAdd(&cnt[0], 1);
+      continue;
+    }
+    for (int t0 = 0; t0 < ctx; t0 += part_tokens) {
+      const int nb = (min(part_tokens, ctx - t0) + BS - 1) / BS;
+      atomicAdd(&cnt[min(nb, PLAN_BUCKETS - 1)], 1);
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int run = 0;
+    for (int b = PLAN_BUCKETS - 1; b >= 0; --b) {
+      const int c = cnt[b];
+      cnt[b] = run;
+      run += c;
+    }
+    a.work_ctrl[0] = 0;
+    a.work_ctrl[1] = run;
+  }
+  __syncthreads();
+  for (int s = threadIdx.x; s < a.num_seqs; s += blockDim.x) {
+    const int ctx = clamp_ctx(a, s);
+    if (ctx <= 0) {
+      a.work_list[atomicAdd(&cnt[0], 1)] = s * a.num_parts;
+      continue;
+    }
+    int p = 0;
+    for (int t0 = 0; t0 < ctx; t0 += part_tokens, ++p) {
+      const int nb = (min(part_tokens, ctx - t0) + BS - 1) / BS;
+      a.work_list[atomicAdd(&cnt[min(nb, PLAN_BUCKETS - 1)], 1)] = s * a.num_parts + p;
+    }
+  }
+}
+
 template <typename E, typename O, int D>
 __global__ __launch_bounds__(NW * 64) void decode_partial_kernel(const DecodeArgs a) {
   using G = DecodeGeom<E, D>;
@@ -60,149 +130,159 @@ __global__ __launch_bounds__(NW * 64) void decode_partial_kernel(const DecodeArg
   __shared__ float sm_m[ROWS];
   __shared__ float sm_l[ROWS];
   __shared__ __attribute__((aligned(16))) float sm_acc[ROWS][D];
-
-  const int wg = blockIdx.x;
-  const int u = (wg & 7) * a.per_xcd + (wg >> 3);
-  if (u >= a.total_units) return;
-  const int p = u % a.num_parts;
-  const int su = u / a.num_parts;
-  const int s = su % a.num_seqs;
-  const int h = su / a.num_seqs;
+  __shared__ int sm_unit[2];
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane / LPT;
   const int c = lane % LPT;
-
-  const int64_t sh = (int64_t)s * a.num_heads + h;
-  const int ctx = min(a.context_lens[s], a.max_context_len);
   const int part_tokens = a.part_blocks * BS;
-  const int tok0 = p * part_tokens;
-  if (ctx <= 0) {  // undefined attention: report NaN rather than garbage
-    if (p == 0 && threadIdx.x < D) Out<O>::put(a.out, sh * D + threadIdx.x, __builtin_nanf(""));
-    return;
-  }
-  if (tok0 >= ctx) return;
-  const int nparts = (ctx + part_tokens - 1) / part_tokens;
-  const int nblk = (min(part_tokens, ctx - tok0) + BS - 1) / BS;
-
-  const uint4 qv = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(a.q) + sh * (D * G::ES) + c * 16);
-
+  const int total = a.work_ctrl[1] * a.num_heads;
   const int64_t bstride = (int64_t)a.num_heads * G::TILE;
-  const char* kbase = reinterpret_cast<const char*>(a.k_cache) + (int64_t)h * G::TILE + lane * 16;
-  const char* vbase = reinterpret_cast<const char*>(a.v_cache) + (int64_t)h * G::TILE + lane * 16;
-  const int32_t* trow = a.block_tables + (int64_t)s * a.max_blocks_per_seq + tok0 / BS;
 
-  float m = NEG_BIG, l = 0.f;
-  float acc[VEC];
-#pragma unroll
-  for (int e = 0; e < VEC; ++e) acc[e] = 0.f;
+  for (int it = 0;; ++it) {
+    // Claim the next unit.  The slot alternates with the iteration, so one
+    // barrier suffices: a slot is rewritten only after every wave has passed
+    // the following iteration's barrier.
+    if (threadIdx.x == 0) sm_unit[it & 1] = atomicAdd(&a.work_ctrl[0], 1);
+    __syncthreads();
+    const int u = __builtin_amdgcn_readfirstlane(sm_unit[it & 1]);
+    if (u >= total) break;
+    const int e = u / a.num_heads;
+    const int h = u - e * a.num_heads;
+    const int entry = a.work_list[e];
+    const int s = entry / a.num_parts;
+    const int p = entry - s * a.num_parts;
 
-  auto load = [&](int phys, uint4 (&kx)[NI], uint4 (&vx)[NI]) {
-    const char* kp = kbase + (int64_t)phys * bstride;
-    const char* vp = vbase + (int64_t)phys * bstride;
-#pragma unroll
-    for (int i = 0; i < NI; ++i) kx[i] = *reinterpret_cast<const uint4*>(kp + i * 1024);
-#pragma unroll
-    for (int i = 0; i < NI; ++i) vx[i] = *reinterpret_cast<const uint4*>(vp + i * 1024);
-  };
+    const int64_t sh = (int64_t)s * a.num_heads + h;
+    const int ctx = clamp_ctx(a, s);
+    const int tok0 = p * part_tokens;
+    if (ctx <= 0) {  // undefined attention: report NaN rather than garbage
+      if (threadIdx.x < D) Out<O>::put(a.out, sh * D + threadIdx.x, __builtin_nanf(""));
+      continue;
+    }
+    if (tok0 >= ctx) continue;
+    const int nparts = (ctx + part_tokens - 1) / part_tokens;
+    const int nblk = (min(part_tokens, ctx - tok0) + BS - 1) / BS;
 
-  auto consume = [&](const uint4 (&kx)[NI], uint4 (&vx)[NI], int jb, bool bad) {
-    const int tb = tok0 + jb * BS;  // position of the block's first token
-    float sc[NI];
+    const uint4 qv = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(a.q) + sh * (D * G::ES) + c * 16);
+    const char* kbase = reinterpret_cast<const char*>(a.k_cache) + (int64_t)h * G::TILE + lane * 16;
+    const char* vbase = reinterpret_cast<const char*>(a.v_cache) + (int64_t)h * G::TILE + lane * 16;
+    const int32_t* trow = a.block_tables + (int64_t)s * a.max_blocks_per_seq + tok0 / BS;
+
+    float m = NEG_BIG, l = 0.f;
+    float acc[VEC];
 #pragma unroll
-    for (int i = 0; i < NI; ++i) sc[i] = group_sum<LPT>(C::dot(qv, kx[i])) * a.scale_log2;
-    if (tb + BS > ctx) {  // partly filled last block
+    for (int e2 = 0; e2 < VEC; ++e2) acc[e2] = 0.f;
+
+    auto load = [&](int phys, uint4 (&kx)[NI], uint4 (&vx)[NI]) {
+      const char* kp = kbase + (int64_t)phys * bstride;
+      const char* vp = vbase + (int64_t)phys * bstride;
+#pragma unroll
+      for (int i = 0; i < NI; ++i) kx[i] = load_kv16(kp + i * 1024);
+#pragma unroll
+      for (int i = 0; i < NI; ++i) vx[i] = load_kv16(vp + i * 1024);
+    };
+
+    auto consume = [&](const uint4 (&kx)[NI], uint4 (&vx)[NI], int jb, bool bad) {
+      const int tb = tok0 + jb * BS;  // position of the block's first token
+      float sc[NI];
+#pragma unroll
+      for (int i = 0; i < NI; ++i) sc[i] = group_sum<LPT>(C::dot(qv, kx[i])) * a.scale_log2;
+      if (tb + BS > ctx) {  // partly filled last block
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+          const bool dead = tb + i * TPI + r >= ctx;
+          sc[i] = dead ? -INFINITY : sc[i];
+          vx[i] = dead ? make_uint4(0u, 0u, 0u, 0u) : vx[i];
+        }
+      }
+      if (bad) {
+#pragma unroll
+        for (int i = 0; i < NI; ++i) sc[i] = __builtin_nanf("");
+      }
+      float mx = m;
+#pragma unroll
+      for (int i = 0; i < NI; ++i) mx = fmaxf(mx, sc[i]);
+      const float alpha = fast_exp2(m - mx);
+      m = mx;
+      l *= alpha;
+#pragma unroll
+      for (int e2 = 0; e2 < VEC; ++e2) acc[e2] *= alpha;
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
-        const bool dead = tb + i * TPI + r >= ctx;
-        sc[i] = dead ? -INFINITY : sc[i];
-        vx[i] = dead ? make_uint4(0u, 0u, 0u, 0u) : vx[i];
+        const float pi = fast_exp2(sc[i] - m);
+        l += pi;
+        float vf[VEC];
+        C::unpack(vx[i], vf);
+#pragma unroll
+        for (int e2 = 0; e2 < VEC; ++e2) acc[e2] = fmaf(pi, vf[e2], acc[e2]);
       }
-    }
-    if (bad) {
-#pragma unroll
-      for (int i = 0; i < NI; ++i) sc[i] = __builtin_nanf("");
-    }
-    float mx = m;
-#pragma unroll
-    for (int i = 0; i < NI; ++i) mx = fmaxf(mx, sc[i]);
-    const float alpha = fast_exp2(m - mx);
-    m = mx;
-    l *= alpha;
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) acc[e] *= alpha;
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const float pi = fast_exp2(sc[i] - m);
-      l += pi;
-      float vf[VEC];
-      C::unpack(vx[i], vf);
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) acc[e] = fmaf(pi, vf[e], acc[e]);
-    }
-  };
-
-  for (int cb = 0; cb < nblk; cb += 64) {
-    const int cn = min(64, nblk - cb);
-    // The chunk's table entries, one per lane; a wave-uniform readlane picks each.
-    const int tv = lane < cn ? trow[cb + lane] : 0;
-    auto phys_of = [&](int j, bool& bad) {
-      const int ph = __builtin_amdgcn_readlane(tv, j);
-      bad = (uint64_t)(uint32_t)ph >= (uint64_t)a.num_blocks;
-      return bad ? 0 : ph;
     };
-    int j = w;
-    if (j >= cn) continue;
-    uint4 kA[NI], vA[NI], kB[NI], vB[NI];
-    bool badA, badB;
-    load(phys_of(j, badA), kA, vA);
-    while (j + 2 * NW < cn) {
-      load(phys_of(j + NW, badB), kB, vB);
-      consume(kA, vA, cb + j, badA);
-      load(phys_of(j + 2 * NW, badA), kA, vA);
-      consume(kB, vB, cb + j + NW, badB);
-      j += 2 * NW;
-    }
-    if (j + NW < cn) {
-      load(phys_of(j + NW, badB), kB, vB);
-      consume(kA, vA, cb + j, badA);
-      consume(kB, vB, cb + j + NW, badB);
-    } else {
-      consume(kA, vA, cb + j, badA);
-    }
-  }
 
-  // Merge the ROWS running states of this partition: max, rescaled sums.
-  if (c == 0) {
-    sm_m[w * TPI + r] = m;
-    sm_l[w * TPI + r] = l;
-  }
-#pragma unroll
-  for (int e = 0; e < VEC; ++e) sm_acc[w * TPI + r][c * VEC + e] = acc[e];
-  __syncthreads();
-  if (threadIdx.x < D) {
-    const int t = threadIdx.x;
-    float M = sm_m[0];
-#pragma unroll
-    for (int k = 1; k < ROWS; ++k) M = fmaxf(M, sm_m[k]);
-    float Ls = 0.f, A = 0.f;
-#pragma unroll
-    for (int k = 0; k < ROWS; ++k) {
-      const float f = fast_exp2(sm_m[k] - M);
-      Ls = fmaf(sm_l[k], f, Ls);
-      A = fmaf(sm_acc[k][t], f, A);
-    }
-    if (nparts == 1) {
-      Out<O>::put(a.out, sh * D + t, A / Ls);
-    } else {
-      const int64_t pi = sh * a.num_parts + p;
-      a.ws_acc[pi * D + t] = A;
-      if (t == 0) {
-        a.ws_ml[pi * 2] = M;
-        a.ws_ml[pi * 2 + 1] = Ls;
+    for (int cb = 0; cb < nblk; cb += 64) {
+      const int cn = min(64, nblk - cb);
+      // The chunk's table entries, one per lane; a wave-uniform readlane picks each.
+      const int tv = lane < cn ? trow[cb + lane] : 0;
+      auto phys_of = [&](int j, bool& bad) {
+        const int ph = __builtin_amdgcn_readlane(tv, j);
+        bad = (uint64_t)(uint32_t)ph >= (uint64_t)a.num_blocks;
+        return bad ? 0 : ph;
+      };
+      int j = w;
+      if (j >= cn) continue;
+      uint4 kA[NI], vA[NI], kB[NI], vB[NI];
+      bool badA, badB;
+      load(phys_of(j, badA), kA, vA);
+      while (j + 2 * NW < cn) {
+        load(phys_of(j + NW, badB), kB, vB);
+        consume(kA, vA, cb + j, badA);
+        load(phys_of(j + 2 * NW, badA), kA, vA);
+        consume(kB, vB, cb + j + NW, badB);
+        j += 2 * NW;
+      }
+      if (j + NW < cn) {
+        load(phys_of(j + NW, badB), kB, vB);
+        consume(kA, vA, cb + j, badA);
+        consume(kB, vB, cb + j + NW, badB);
+      } else {
+        consume(kA, vA, cb + j, badA);
       }
     }
+
+    // Merge the ROWS running states of this unit: max, rescaled sums.
+    if (c == 0) {
+      sm_m[w * TPI + r] = m;
+      sm_l[w * TPI + r] = l;
+    }
+#pragma unroll
+    for (int e2 = 0; e2 < VEC; ++e2) sm_acc[w * TPI + r][c * VEC + e2] = acc[e2];
+    __syncthreads();
+    if (threadIdx.x < D) {
+      const int t = threadIdx.x;
+      float M = sm_m[0];
+#pragma unroll
+      for (int k = 1; k < ROWS; ++k) M = fmaxf(M, sm_m[k]);
+      float Ls = 0.f, A = 0.f;
+#pragma unroll
+      for (int k = 0; k < ROWS; ++k) {
+        const float f = fast_exp2(sm_m[k] - M);
+        Ls = fmaf(sm_l[k], f, Ls);
+        A = fmaf(sm_acc[k][t], f, A);
+      }
+      if (nparts == 1) {
+        Out<O>::put(a.out, sh * D + t, A / Ls);
+      } else {
+        const int64_t pi = sh * a.num_parts + p;
+        a.ws_acc[pi * D + t] = A;
+        if (t == 0) {
+          a.ws_ml[pi * 2] = M;
+          a.ws_ml[pi * 2 + 1] = Ls;
+        }
+      }
+    }
+    // The next unit's LDS writes come after the next claim barrier, which every
+    // thread reaches only after finishing the merge above.
   }
 }
 
@@ -213,7 +293,7 @@ template <typename O, int D>
 __global__ __launch_bounds__(D) void decode_reduce_kernel(const DecodeArgs a) {
   const int s = blockIdx.x;
   const int h = blockIdx.y;
-  const int ctx = min(a.context_lens[s], a.max_context_len);
+  const int ctx = clamp_ctx(a, s);
   if (ctx <= 0) return;
   const int part_tokens = a.part_blocks * BS;
   const int nparts = (ctx + part_tokens - 1) / part_tokens;
@@ -232,9 +312,30 @@ __global__ __launch_bounds__(D) void decode_reduce_kernel(const DecodeArgs a) {
   Out<O>::put(a.out, sh * D + t, A / Ls);
 }
 
+// Workgroups of the persistent kernel: enough to fill every CU of the device
+// at the kernel's occupancy, never more than there are units.
+template <typename K>
+static int persistent_grid(K kernel, int block, int64_t units) {
+  constexpr int kMaxDev = 64;
+  static int slots[kMaxDev];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+  int n = dev < kMaxDev ? slots[dev] : 0;
+  if (n == 0) {
+    int cus = 0, occ = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, block, 0) != hipSuccess || occ <= 0) occ = 1;
+    n = cus * occ;
+    if (dev < kMaxDev) slots[dev] = n;
+  }
+  return (int)(units < n ? units : n);
+}
+
 template <typename E, typename O, int D>
 static hipError_t partial_t(const DecodeArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL((decode_partial_kernel<E, O, D>), dim3(a.per_xcd * 8), dim3(NW * 64), 0, st, a);
+  hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(1024), 0, st, a);
+  const int grid = persistent_grid(decode_partial_kernel<E, O, D>, NW * 64, a.total_units);
+  hipLaunchKernelGGL((decode_partial_kernel<E, O, D>), dim3(grid), dim3(NW * 64), 0, st, a);
   return hipGetLastError();
 }
 

@@ -60,11 +60,19 @@ bool copy_to_host(std::vector<T>& dst, const T* src, size_t n, hipStream_t st) {
   return hipStreamSynchronize(st) == hipSuccess;
 }
 
+// Decode workspace, in this order (each region 16-byte aligned):
+//   work_ctrl  2 int32 (+ padding to 16 bytes)
+//   work_list  S * P int32
+//   ws_acc     S * H * P * D float   (only when P > 1)
+//   ws_ml      S * H * P * 2 float   (only when P > 1)
 struct DecodePlan {
   int32_t part_blocks = 0;
   int32_t num_parts = 0;
+  size_t list_off = 0, acc_off = 0, ml_off = 0;
   size_t ws_bytes = 0;
 };
+
+size_t align16(size_t x) { return (x + 15) & ~(size_t)15; }
 
 DecodePlan plan_decode(int32_t num_seqs, int32_t num_heads, int32_t head_dim, int32_t max_context_len,
                        int32_t partition_size) {
@@ -76,8 +84,11 @@ DecodePlan plan_decode(int32_t num_seqs, int32_t num_heads, int32_t head_dim, in
     p.part_blocks = partition_size / kBlock;
     p.num_parts = (max_context_len + partition_size - 1) / partition_size;
   }
-  if (p.num_parts > 1)
-    p.ws_bytes = (size_t)num_seqs * num_heads * p.num_parts * ((size_t)head_dim + 2) * sizeof(float);
+  const size_t units = (size_t)num_seqs * num_heads * p.num_parts;
+  p.list_off = 16;
+  p.acc_off = p.list_off + align16((size_t)num_seqs * p.num_parts * sizeof(int32_t));
+  p.ml_off = p.acc_off + (p.num_parts > 1 ? units * head_dim * sizeof(float) : 0);
+  p.ws_bytes = p.ml_off + (p.num_parts > 1 ? units * 2 * sizeof(float) : 0);
   return p;
 }
 
@@ -102,10 +113,8 @@ int decode_impl(int stages, const void* q, const void* k_cache, const void* v_ca
   const int64_t units = (int64_t)num_seqs * desc->num_heads * plan.num_parts;
   if (units > ((int64_t)1 << 31) - 64 || num_seqs > 65535 * 32768) return PKV_EINVAL;
   if (desc->num_heads > 65535) return PKV_EINVAL;
-  if (plan.ws_bytes > 0) {
-    if (workspace == nullptr || !aligned(workspace, 16)) return PKV_EINVAL;
-    if (workspace_bytes < plan.ws_bytes) return PKV_EWORKSPACE;
-  }
+  if (workspace == nullptr || !aligned(workspace, 16)) return PKV_EINVAL;
+  if (workspace_bytes < plan.ws_bytes) return PKV_EWORKSPACE;
   st = device_status();
   if (st != PKV_OK) return st;
   hipStream_t sm = reinterpret_cast<hipStream_t>(stream);
@@ -131,8 +140,11 @@ int decode_impl(int stages, const void* q, const void* k_cache, const void* v_ca
   a.block_tables = block_tables;
   a.context_lens = context_lens;
   a.out = out;
-  a.ws_acc = reinterpret_cast<float*>(workspace);
-  a.ws_ml = plan.ws_bytes ? a.ws_acc + (size_t)num_seqs * desc->num_heads * plan.num_parts * desc->head_dim : nullptr;
+  char* ws = reinterpret_cast<char*>(workspace);
+  a.work_ctrl = reinterpret_cast<int32_t*>(ws);
+  a.work_list = reinterpret_cast<int32_t*>(ws + plan.list_off);
+  a.ws_acc = plan.num_parts > 1 ? reinterpret_cast<float*>(ws + plan.acc_off) : nullptr;
+  a.ws_ml = plan.num_parts > 1 ? reinterpret_cast<float*>(ws + plan.ml_off) : nullptr;
   a.num_blocks = desc->num_blocks;
   a.num_heads = desc->num_heads;
   a.max_blocks_per_seq = max_blocks_per_seq;
@@ -141,7 +153,6 @@ int decode_impl(int stages, const void* q, const void* k_cache, const void* v_ca
   a.part_blocks = plan.part_blocks;
   a.num_parts = plan.num_parts;
   a.total_units = (int32_t)units;
-  a.per_xcd = (int32_t)((units + 7) / 8);
   a.scale_log2 = scale * 1.4426950408889634f;
 
   if (stages & kPartial) {

@@ -28,8 +28,10 @@ struct DecodeArgs {
   const int32_t* block_tables;
   const int32_t* context_lens;
   void* out;
-  float* ws_acc;  // [S][H][P][D] unnormalised partial outputs
-  float* ws_ml;   // [S][H][P][2]  running max (log2 units) and sum
+  float* ws_acc;      // [S][H][P][D] unnormalised partial outputs
+  float* ws_ml;       // [S][H][P][2]  running max (log2 units) and sum
+  int32_t* work_list; // [S*P] (sequence, partition) entries, largest partitions first
+  int32_t* work_ctrl; // [0] next unit to claim, [1] number of entries in work_list
   int64_t num_blocks;
   int32_t num_heads;
   int32_t max_blocks_per_seq;
@@ -37,8 +39,7 @@ struct DecodeArgs {
   int32_t max_context_len;
   int32_t part_blocks;  // blocks per partition
   int32_t num_parts;    // P: partitions of the longest allowed context
-  int32_t per_xcd;      // workgroups per XCD slice of the grid
-  int32_t total_units;  // H * S * P
+  int32_t total_units;  // upper bound on units: H * S * P
   float scale_log2;     // scale * log2(e)
 };
 

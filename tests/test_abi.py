@@ -56,10 +56,12 @@ def test_version_and_status_strings(lib):
 
 
 def test_workspace_sizing(lib):
-    # 256 seqs x 32 heads x ceil(4096/512)=8 partitions x (128 + 2) floats
-    assert lib.pkv_decode_workspace_bytes(256, 32, 128, 4096, 512) == 256 * 32 * 8 * 130 * 4
-    assert lib.pkv_decode_workspace_bytes(256, 32, 128, 512, 512) == 0  # one partition: no split
-    assert lib.pkv_decode_workspace_bytes(256, 32, 128, 4096, 0) == 0   # split disabled
+    # counter (16 B) + unit list (256 seqs x 8 partitions int32) + partials
+    # (256 seqs x 32 heads x ceil(4096/512)=8 partitions x (128 + 2) floats)
+    assert lib.pkv_decode_workspace_bytes(256, 32, 128, 4096, 512) == 16 + 256 * 8 * 4 + 256 * 32 * 8 * 130 * 4
+    assert lib.pkv_decode_workspace_bytes(256, 32, 128, 512, 512) == 16 + 256 * 4  # one partition: no partials
+    assert lib.pkv_decode_workspace_bytes(256, 32, 128, 4096, 0) == 16 + 256 * 4   # split disabled
+    assert lib.pkv_decode_workspace_bytes(3, 32, 128, 4096, 512) == 16 + 96 + 3 * 32 * 8 * 130 * 4
     assert lib.pkv_decode_workspace_bytes(0, 32, 128, 4096, 512) == 0
 
 
