@@ -40,7 +40,10 @@ METRIC = "paged decode attention: KV HBM GB/s (% of peak) + tokens attended/s"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "paged_decode_pmc.txt")
-DECODE_SOURCE = os.path.join(ROOT, "paged_kv_cache_137_amd", "csrc", "paged_decode.hip")
+# The decode kernel's source and the headers it includes: the counter-derived
+# traffic is reported only while these are unchanged.
+DECODE_SOURCES = [os.path.join(ROOT, "paged_kv_cache_137_amd", "csrc", f)
+                  for f in ("paged_decode.hip", "pkv_device.h", "pkv_internal.h")]
 
 
 def _args():
@@ -57,9 +60,12 @@ def _args():
     return ap.parse_args()
 
 
-def source_digest(path: str = DECODE_SOURCE) -> str:
-    with open(path, "rb") as f:
-        return hashlib.sha1(f.read()).hexdigest()[:12]
+def source_digest(paths=DECODE_SOURCES) -> str:
+    h = hashlib.sha1()
+    for path in paths:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:12]
 
 
 def read_pmc_summary():

@@ -203,7 +203,7 @@ int pkv_paged_attn_decode_reduce(const void* q, const void* k_cache, const void*
  *   prompt_lens    int32 [num_prompts], each in [0, max_prompt_len]; their sum
  *                  must equal total_tokens.  Rows beyond total_tokens are never
  *                  touched.
- *   scale          multiplies q.k (usually 1/sqrt(head_dim))
+ *   scale          multiplies q.k (usually 1/sqrt(head_dim)); must be positive and finite
  *   out            [total_tokens][num_heads][head_dim] of out_dtype (PKV_F32 or `dtype`)
  */
 int pkv_paged_attn_prefill(const void* q, const void* k, const void* v, int32_t num_heads, int32_t head_dim,

@@ -9,6 +9,14 @@
 // Design for CDNA4 (the pages give no kernel for this step):
 //  - Workgroup = 4 wavefronts = 128 query rows of one (prompt, head).  Each wave
 //    owns 32 queries.  Key/value tiles of 64 rows are staged in LDS and shared.
+//    LDS is double-buffered: the next tile's K/V are loaded from HBM into
+//    registers before the current tile's products, and stored to the other
+//    buffer after them, so HBM latency hides behind the matrix cores.  There is
+//    one barrier per tile.
+//  - A 64-key tile's two 32-key score chains are issued together, so their
+//    MFMAs interleave.  Each half-wave keeps a lane-local partial row sum
+//    against a shared reference maximum.  The halves exchange only when that
+//    reference moves (rarely), and once at the end.
 //  - Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16 on
 //    16-bit inputs and fp32 accumulation.  Each lane's 16 accumulator values
 //    then belong to a single query (its column).  The online softmax (running
@@ -19,18 +27,27 @@
 //    directly.  Its key order inside an MFMA k-step follows the accumulator
 //    layout.  V^T is read from LDS in that same key order.  V is written into
 //    LDS transposed ([dim][key]) when it is staged.
-//  - Probabilities are rounded once to the input type for the MFMA.  The row
-//    sum adds the rounded values, so the normalisation matches what was
-//    accumulated.
+//  - Probabilities are exp2(s * scale * log2 e - m): one FMA and one v_exp each.
+//    They are rounded once to the input type for the MFMA.  The row sum adds
+//    the rounded values (v_dot2 against ones), so the normalisation matches
+//    what was accumulated.  The reference maximum m moves only when a row's
+//    maximum rises by more than 8 (log2 units).  Probabilities then stay below
+//    2^8, and the 64-value accumulator rescale is rare.
 //  - Causality: key tiles past the workgroup's last query are never loaded.
 //    Key tiles past a wave's last query are skipped by that wave.  Tiles that
 //    straddle the diagonal or the prompt end are masked by selecting -inf.
 //  - Query tiles are dispatched longest-first (descending tile index), to even
 //    out the causal triangle's load.
+#include <type_traits>
+
 #include "pkv_device.h"
 #include "pkv_internal.h"
 
 namespace pkv {
+
+#ifndef PKV_PRE_XCD
+#define PKV_PRE_XCD 1
+#endif
 
 template <typename E>
 __device__ __forceinline__ f32x16_t mfma32(const uint4& a, const uint4& b, const f32x16_t& c);
@@ -59,45 +76,77 @@ __device__ __forceinline__ uint32_t pack2<f16_t>(float lo, float hi) {
   v.y = (_Float16)hi;
   return __builtin_bit_cast(uint32_t, v);
 }
-template <typename E> __device__ __forceinline__ float sum2(uint32_t w);
-template <> __device__ __forceinline__ float sum2<bf16_t>(uint32_t w) { return bf16_lo(w) + bf16_hi(w); }
-template <> __device__ __forceinline__ float sum2<f16_t>(uint32_t w) { return f16_lo(w) + f16_hi(w); }
+// acc + both halves of a packed pair, as one v_dot2 against (1, 1).
+template <typename E> __device__ __forceinline__ float rowsum2(uint32_t w, float acc);
+template <>
+__device__ __forceinline__ float rowsum2<bf16_t>(uint32_t w, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w), __builtin_bit_cast(bf16x2_t, 0x3f803f80u), acc, false);
+}
+template <>
+__device__ __forceinline__ float rowsum2<f16_t>(uint32_t w, float acc) {
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, w), __builtin_bit_cast(f16x2_t, 0x3c003c00u), acc, false);
+}
 
+// Store four outputs x * inv.  The product is rounded to float32 first (no
+// contraction), and a 16-bit output is that float rounded to nearest even.
 template <typename O> struct Store4;
 template <> struct Store4<f32_t> {
-  __device__ __forceinline__ static void put(void* base, int64_t i, float a, float b, float c, float d) {
-    *reinterpret_cast<float4*>(reinterpret_cast<float*>(base) + i) = make_float4(a, b, c, d);
+  __device__ __forceinline__ static void put(void* base, int64_t i, float a, float b, float c, float d, float inv) {
+#pragma clang fp contract(off)
+    *reinterpret_cast<float4*>(reinterpret_cast<float*>(base) + i) = make_float4(a * inv, b * inv, c * inv, d * inv);
   }
 };
 template <> struct Store4<bf16_t> {
-  __device__ __forceinline__ static void put(void* base, int64_t i, float a, float b, float c, float d) {
-    const uint32_t x = (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
-    const uint32_t y = (uint32_t)f32_to_bf16(c) | ((uint32_t)f32_to_bf16(d) << 16);
-    *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(base) + i) = make_uint2(x, y);
+  __device__ __forceinline__ static void put(void* base, int64_t i, float a, float b, float c, float d, float inv) {
+#pragma clang fp contract(off)
+    float ra = a * inv, rb = b * inv, rc = c * inv, rd = d * inv;
+    asm volatile("" : "+v"(ra), "+v"(rb), "+v"(rc), "+v"(rd));
+    // v_cvt_pk_bf16_f32: round to nearest even
+    *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(base) + i) = make_uint2(pack2<bf16_t>(ra, rb), pack2<bf16_t>(rc, rd));
   }
 };
 template <> struct Store4<f16_t> {
-  __device__ __forceinline__ static void put(void* base, int64_t i, float a, float b, float c, float d) {
-    const uint32_t x = (uint32_t)f32_to_f16_bits(a) | ((uint32_t)f32_to_f16_bits(b) << 16);
-    const uint32_t y = (uint32_t)f32_to_f16_bits(c) | ((uint32_t)f32_to_f16_bits(d) << 16);
+  __device__ __forceinline__ static void put(void* base, int64_t i, float a, float b, float c, float d, float inv) {
+#pragma clang fp contract(off)
+    const float ra = a * inv, rb = b * inv, rc = c * inv, rd = d * inv;
+    const uint32_t x = (uint32_t)f32_to_f16_bits(ra) | ((uint32_t)f32_to_f16_bits(rb) << 16);
+    const uint32_t y = (uint32_t)f32_to_f16_bits(rc) | ((uint32_t)f32_to_f16_bits(rd) << 16);
     *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(base) + i) = make_uint2(x, y);
   }
 };
 
 template <typename E, typename O, int D>
-__global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs a) {
-  constexpr int BM = PREFILL_BLOCK_M;  // query rows per workgroup (4 waves x 32)
-  constexpr int BN = 64;               // keys per LDS tile
-  constexpr int KS = D / 16;           // k-steps of Q K^T
-  constexpr int DB = D / 32;           // 32-row blocks of O^T
-  constexpr int KROW = D * 2 + 16;     // LDS bytes per K row, padded against bank conflicts
-  constexpr int VROW = BN * 2 + 8;     // LDS bytes per V^T row, padded likewise
-  __shared__ __attribute__((aligned(16))) unsigned char k_lds[BN * KROW];
-  __shared__ __attribute__((aligned(16))) unsigned char v_lds[D * VROW];
+__global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
+  constexpr int BM = PREFILL_BLOCK_M;      // query rows per workgroup (4 waves x 32)
+  constexpr int BN = 64;                   // keys per LDS tile
+  constexpr int KS = D / 16;               // k-steps of Q K^T
+  constexpr int DB = D / 32;               // 32-row blocks of O^T
+  constexpr int KROW = D * 2 + 16;         // LDS bytes per K row, padded against bank conflicts
+  constexpr int VROW = BN * 2 + 8;         // LDS bytes per V^T row, padded likewise
+  constexpr int KCH = BN * (D / 8) / 256;  // 16-byte K chunks each thread stages per tile
+  constexpr int VG = (BN / 4) * (D / 8);   // (4 keys x 8 dims) V groups per tile
+  constexpr float RESCALE_SLACK = 8.0f;    // log2 units a row maximum may rise before rescaling
+  static_assert(KCH * 256 == BN * (D / 8) && VG <= 256, "staging must map onto 256 threads");
+  // Two LDS buffers: tile n is read from one while tile n+1 is written to the other.
+  __shared__ __attribute__((aligned(16))) unsigned char k_lds[2][BN * KROW];
+  __shared__ __attribute__((aligned(16))) unsigned char v_lds[2][D * VROW];
 
-  const int qt = a.num_qtiles - 1 - (int)blockIdx.x;
-  const int h = blockIdx.y;
-  const int pr = blockIdx.z;
+  // Work item w enumerates (head, prompt, query tile), tile fastest and longest
+  // first.  With the XCD remap, each XCD walks a contiguous range of w.  All
+  // query tiles of a (prompt, head) then share one XCD's L2, which holds the
+  // K/V they all reread.
+  const int wg = blockIdx.x;
+#if PKV_PRE_XCD
+  const int wi = (wg & 7) * a.per_xcd + (wg >> 3);
+#else
+  const int wi = wg;
+#endif
+  if (wi >= a.total_items) return;
+  const int t = wi % a.num_qtiles;
+  const int rest = wi / a.num_qtiles;
+  const int pr = rest % a.num_prompts;
+  const int h = rest / a.num_prompts;
+  const int qt = a.num_qtiles - 1 - t;
   const int m0 = qt * BM;
   int L = a.prompt_lens[pr];
   if (L <= m0) return;
@@ -116,21 +165,86 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs a) {
   const int hf = lane >> 5;
   const int qrow0 = m0 + w * 32;  // first query of this wave
   const int qi = qrow0 + ql;      // this lane's query
-  const int64_t rs = (int64_t)a.num_heads * D;
-  const uint16_t* qb = reinterpret_cast<const uint16_t*>(a.q) + off * rs + (int64_t)h * D;
-  const uint16_t* kb = reinterpret_cast<const uint16_t*>(a.k) + off * rs + (int64_t)h * D;
-  const uint16_t* vb = reinterpret_cast<const uint16_t*>(a.v) + off * rs + (int64_t)h * D;
+  const int64_t rs = (int64_t)a.num_heads * D;  // elements between consecutive tokens
+  const uint32_t rsb = (uint32_t)(rs * 2);       // the same, in bytes
+  const char* qb = reinterpret_cast<const char*>(a.q) + (off * rs + (int64_t)h * D) * 2;
+  const char* kb = reinterpret_cast<const char*>(a.k) + (off * rs + (int64_t)h * D) * 2;
+  const char* vb = reinterpret_cast<const char*>(a.v) + (off * rs + (int64_t)h * D) * 2;
+  const float c = a.scale_log2;  // > 0
 
   // Q as the B operand of S^T = K Q^T: k-step kk holds dims kk*16 + hf*8 .. +8.
   uint4 qf[KS];
   if (qi < L) {
-    const uint16_t* qp = qb + (int64_t)qi * rs + hf * 8;
+    const char* qp = qb + (int64_t)qi * rsb + hf * 16;
 #pragma unroll
-    for (int kk = 0; kk < KS; ++kk) qf[kk] = *reinterpret_cast<const uint4*>(qp + kk * 16);
+    for (int kk = 0; kk < KS; ++kk) qf[kk] = *reinterpret_cast<const uint4*>(qp + kk * 32);
   } else {
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) qf[kk] = make_uint4(0u, 0u, 0u, 0u);
   }
+
+  // Per-thread staging slots (fixed for the whole loop): K chunk i is row
+  // krow[i], chunk kch[i] of the tile; the V group is keys 4*vg..+3, dims vch*8..+7.
+  int krow[KCH];
+  uint32_t koff[KCH], klds[KCH];
+#pragma unroll
+  for (int i = 0; i < KCH; ++i) {
+    const int idx = threadIdx.x + i * 256;
+    krow[i] = idx / (D / 8);
+    const int ch = idx % (D / 8);
+    koff[i] = krow[i] * rsb + ch * 16;
+    klds[i] = krow[i] * KROW + ch * 16;
+  }
+  const int vg = threadIdx.x % (BN / 4), vch = threadIdx.x / (BN / 4);
+  const uint32_t voff = 4 * vg * rsb + vch * 16;
+  const uint32_t vlds = (vch * 8) * VROW + vg * 8;
+
+  // Staging registers: the next tile's K chunks and V group, loaded from HBM
+  // while the current tile is being multiplied.
+  struct Stage {
+    uint4 k[KCH];
+    uint4 v[4];
+  };
+  Stage sa;
+  auto gload = [&](Stage& st_, int n0) {
+    uint4 (&kst)[KCH] = st_.k;
+    uint4 (&vst)[4] = st_.v;
+    const char* kt = kb + (int64_t)n0 * rsb;
+    const char* vt = vb + (int64_t)n0 * rsb;
+#pragma unroll
+    for (int i = 0; i < KCH; ++i)
+      kst[i] = n0 + krow[i] < L ? *reinterpret_cast<const uint4*>(kt + koff[i]) : make_uint4(0u, 0u, 0u, 0u);
+    if (threadIdx.x < VG) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        vst[i] = n0 + 4 * vg + i < L ? *reinterpret_cast<const uint4*>(vt + voff + i * rsb)
+                                     : make_uint4(0u, 0u, 0u, 0u);
+    }
+  };
+  // K row-major [key][dim]; V transposed to [dim][key], 4 keys per 8-byte store.
+  auto lstore = [&](const Stage& st_, int buf) {
+    const uint4 (&kst)[KCH] = st_.k;
+    const uint4 (&vst)[4] = st_.v;
+#pragma unroll
+    for (int i = 0; i < KCH; ++i) *reinterpret_cast<uint4*>(k_lds[buf] + klds[i]) = kst[i];
+    if (threadIdx.x < VG) {
+      const uint32_t w0[4] = {vst[0].x, vst[0].y, vst[0].z, vst[0].w};
+      const uint32_t w1[4] = {vst[1].x, vst[1].y, vst[1].z, vst[1].w};
+      const uint32_t w2[4] = {vst[2].x, vst[2].y, vst[2].z, vst[2].w};
+      const uint32_t w3[4] = {vst[3].x, vst[3].y, vst[3].z, vst[3].w};
+#pragma unroll
+      for (int qd = 0; qd < 4; ++qd) {  // dword qd holds dims vch*8 + 2qd and 2qd+1
+        // v_perm picks 16-bit halves: 0x05040100 = (low of src1, low of src0),
+        // 0x07060302 = (high of src1, high of src0).
+        const uint2 even = make_uint2(__builtin_amdgcn_perm(w1[qd], w0[qd], 0x05040100u),
+                                      __builtin_amdgcn_perm(w3[qd], w2[qd], 0x05040100u));
+        const uint2 odd = make_uint2(__builtin_amdgcn_perm(w1[qd], w0[qd], 0x07060302u),
+                                     __builtin_amdgcn_perm(w3[qd], w2[qd], 0x07060302u));
+        *reinterpret_cast<uint2*>(v_lds[buf] + vlds + (2 * qd) * VROW) = even;
+        *reinterpret_cast<uint2*>(v_lds[buf] + vlds + (2 * qd + 1) * VROW) = odd;
+      }
+    }
+  };
 
   f32x16_t o[DB];
 #pragma unroll
@@ -138,121 +252,122 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs a) {
 #pragma unroll
     for (int j = 0; j < 16; ++j) o[db][j] = 0.f;
   float mrow = NEG_BIG, lrow = 0.f;
+  const int lim = min(qi, L - 1);  // last key this query may see
 
   const int kend = min(L, m0 + BM);     // keys any query of the workgroup sees
   const int wkend = min(L, qrow0 + 32); // keys any query of this wave sees
 
-  for (int n0 = 0; n0 < kend; n0 += BN) {
-    __syncthreads();  // the previous tile's LDS reads are finished
-    // K tile, row-major [key][dim]; rows past the prompt are zero.
-    for (int idx = threadIdx.x; idx < BN * (D / 8); idx += 256) {
-      const int row = idx / (D / 8), ch = idx % (D / 8);
-      uint4 val = make_uint4(0u, 0u, 0u, 0u);
-      if (n0 + row < L) val = *reinterpret_cast<const uint4*>(kb + (int64_t)(n0 + row) * rs + ch * 8);
-      *reinterpret_cast<uint4*>(k_lds + row * KROW + ch * 16) = val;
-    }
-    // V tile, transposed to [dim][key]: each thread moves 4 keys x 8 dims.
-    for (int idx = threadIdx.x; idx < (BN / 4) * (D / 8); idx += 256) {
-      const int g = idx % (BN / 4), ch = idx / (BN / 4);
-      uint4 rr[4];
+  // One 64-key tile from LDS buffer `buf`, starting at key n0, as NSUB (1 or 2)
+  // sub-tiles of 32 keys.  The sub-tiles' score chains are independent, so
+  // their MFMAs interleave.  Lane (ql, hf) score element j of sub-tile u is key
+  // n0 + 32u + 8*(j/4) + 4*hf + j%4 against query qi.
+  //
+  // The two half-waves hold different keys of the same queries.  Each keeps a
+  // lane-local partial row sum against a shared reference maximum mrow.  They
+  // exchange values only when mrow must move: when some row's maximum rises by
+  // more than the slack.
+  auto tile = [&](auto nsub_c, int buf, int n0) {
+    constexpr int NSUB = decltype(nsub_c)::value;
+    f32x16_t st[NSUB];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = n0 + 4 * g + i;
-        rr[i] = key < L ? *reinterpret_cast<const uint4*>(vb + (int64_t)key * rs + ch * 8) : make_uint4(0u, 0u, 0u, 0u);
+    for (int u = 0; u < NSUB; ++u)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) st[u][j] = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk)
+#pragma unroll
+      for (int u = 0; u < NSUB; ++u) {
+        const unsigned char* kr = k_lds[buf] + (u * 32 + ql) * KROW + hf * 16;
+        st[u] = mfma32<E>(*reinterpret_cast<const uint4*>(kr + kk * 32), qf[kk], st[u]);
       }
-      const uint32_t w0[4] = {rr[0].x, rr[0].y, rr[0].z, rr[0].w};
-      const uint32_t w1[4] = {rr[1].x, rr[1].y, rr[1].z, rr[1].w};
-      const uint32_t w2[4] = {rr[2].x, rr[2].y, rr[2].z, rr[2].w};
-      const uint32_t w3[4] = {rr[3].x, rr[3].y, rr[3].z, rr[3].w};
+
+    if ((n0 + 32 * NSUB - 1 > qrow0) || (n0 + 32 * NSUB > L)) {  // straddles the diagonal or the prompt end
 #pragma unroll
-      for (int qd = 0; qd < 4; ++qd) {  // dword qd holds dims ch*8 + 2qd and 2qd+1
-        const uint2 even = make_uint2((w0[qd] & 0xffffu) | (w1[qd] << 16), (w2[qd] & 0xffffu) | (w3[qd] << 16));
-        const uint2 odd = make_uint2((w0[qd] >> 16) | (w1[qd] & 0xffff0000u), (w2[qd] >> 16) | (w3[qd] & 0xffff0000u));
-        *reinterpret_cast<uint2*>(v_lds + (ch * 8 + 2 * qd) * VROW + g * 8) = even;
-        *reinterpret_cast<uint2*>(v_lds + (ch * 8 + 2 * qd + 1) * VROW + g * 8) = odd;
+      for (int u = 0; u < NSUB; ++u) {
+        const int room = lim - (n0 + 32 * u + 4 * hf);  // element j is visible iff its offset <= room
+#pragma unroll
+        for (int j = 0; j < 16; ++j) st[u][j] = (8 * (j >> 2) + (j & 3) > room) ? -INFINITY : st[u][j];
       }
     }
-    __syncthreads();
-    if (n0 >= wkend) continue;  // every key of this tile is in this wave's future
-
-    // S^T for two 32-key sub-tiles.  Lane (ql, hf) element j is key
-    // n0 + sub*32 + 8*(j/4) + 4*hf + j%4 against query qi.
-    f32x16_t st[2];
+    float lmax = st[0][0];
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
+    for (int u = 0; u < NSUB; ++u)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) st[sub][j] = 0.f;
-      const unsigned char* kr = k_lds + (sub * 32 + ql) * KROW + hf * 16;
+      for (int j = 0; j < 16; ++j) lmax = fmaxf(lmax, st[u][j]);
+    const float mt = lmax * c;  // this half's maximum over the tile, log2 units
+    if (__any(mt > mrow + RESCALE_SLACK)) {
+      const float mnew = fmaxf(mrow, fmaxf(mt, __shfl_xor(mt, 32, 64)));
+      const float alpha = fast_exp2(mrow - mnew);
+      lrow *= alpha;
 #pragma unroll
-      for (int kk = 0; kk < KS; ++kk) st[sub] = mfma32<E>(*reinterpret_cast<const uint4*>(kr + kk * 32), qf[kk], st[sub]);
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) o[db][j] *= alpha;
+      mrow = mnew;
     }
 
-    const bool need_mask = (n0 + BN - 1 > qrow0) || (n0 + BN > L);
-    float mx = mrow;
+    uint32_t pk[NSUB][8];
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        float x = st[sub][j] * a.scale_log2;
-        if (need_mask) {
-          const int key = n0 + sub * 32 + 8 * (j >> 2) + 4 * hf + (j & 3);
-          x = (key > qi || key >= L) ? -INFINITY : x;
-        }
-        st[sub][j] = x;
-        mx = fmaxf(mx, x);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float alpha = fast_exp2(mrow - mx);
-    mrow = mx;
-
-    uint32_t pk[2][8];
-    float ps = 0.f;
-#pragma unroll
-    for (int sub = 0; sub < 2; ++sub)
+    for (int u = 0; u < NSUB; ++u)
 #pragma unroll
       for (int jj = 0; jj < 8; ++jj) {
-        pk[sub][jj] = pack2<E>(fast_exp2(st[sub][2 * jj] - mx), fast_exp2(st[sub][2 * jj + 1] - mx));
-        ps += sum2<E>(pk[sub][jj]);
+        pk[u][jj] = pack2<E>(fast_exp2(fmaf(st[u][2 * jj], c, -mrow)), fast_exp2(fmaf(st[u][2 * jj + 1], c, -mrow)));
+        lrow = rowsum2<E>(pk[u][jj], lrow);
       }
-    ps += __shfl_xor(ps, 32, 64);
-    lrow = lrow * alpha + ps;
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) o[db][j] *= alpha;
 
-    // O^T += V^T P^T over k-steps of 16 keys.  In step kk2, element i of lane
-    // (ql, hf) stands for key n0 + 16*kk2 + 8*(i/4) + 4*hf + i%4, on both operands.
+    // O^T += V^T P^T in k-steps of 16 keys.  In step (u, kk2), element i of lane
+    // (ql, hf) stands for key n0 + 32u + 16*kk2 + 8*(i/4) + 4*hf + i%4 on both operands.
 #pragma unroll
-    for (int kk2 = 0; kk2 < BN / 16; ++kk2) {
-      const int sub = kk2 >> 1, hh = (kk2 & 1) * 4;
-      const uint4 pb = make_uint4(pk[sub][hh], pk[sub][hh + 1], pk[sub][hh + 2], pk[sub][hh + 3]);
+    for (int u = 0; u < NSUB; ++u)
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const unsigned char* vr = v_lds + (db * 32 + ql) * VROW;
-        const uint2 lo = *reinterpret_cast<const uint2*>(vr + (16 * kk2 + 4 * hf) * 2);
-        const uint2 hi = *reinterpret_cast<const uint2*>(vr + (16 * kk2 + 8 + 4 * hf) * 2);
-        o[db] = mfma32<E>(make_uint4(lo.x, lo.y, hi.x, hi.y), pb, o[db]);
+      for (int kk2 = 0; kk2 < 2; ++kk2) {
+        const uint4 pb = make_uint4(pk[u][4 * kk2], pk[u][4 * kk2 + 1], pk[u][4 * kk2 + 2], pk[u][4 * kk2 + 3]);
+        const int kb0 = u * 32 + 16 * kk2 + 4 * hf;  // key within the LDS tile
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const unsigned char* vr = v_lds[buf] + (db * 32 + ql) * VROW;
+          const uint2 lo = *reinterpret_cast<const uint2*>(vr + kb0 * 2);
+          const uint2 hi = *reinterpret_cast<const uint2*>(vr + (kb0 + 8) * 2);
+          o[db] = mfma32<E>(make_uint4(lo.x, lo.y, hi.x, hi.y), pb, o[db]);
+        }
       }
-    }
+  };
+  auto run_tile = [&](int buf, int n0) {
+    if (n0 >= wkend) return;  // every key of the tile is in this wave's future
+    if (n0 + 32 < wkend) tile(std::integral_constant<int, 2>(), buf, n0);
+    else tile(std::integral_constant<int, 1>(), buf, n0);
+  };
+
+  gload(sa, 0);
+  lstore(sa, 0);
+  __syncthreads();
+  int buf = 0;
+  for (int n0 = 0; n0 < kend; n0 += BN, buf ^= 1) {
+    const bool more = n0 + BN < kend;
+    if (more) gload(sa, n0 + BN);
+    run_tile(buf, n0);
+    if (more) lstore(sa, buf ^ 1);
+    __syncthreads();
   }
+  lrow += __shfl_xor(lrow, 32, 64);  // the two halves' partial row sums
 
   if (qi < L) {
+    const float inv = 1.0f / lrow;
     const int64_t ob = (off + qi) * rs + (int64_t)h * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int grp = 0; grp < 4; ++grp) {
         const int d0 = db * 32 + 8 * grp + 4 * hf;
-        Store4<O>::put(a.out, ob + d0, o[db][4 * grp] / lrow, o[db][4 * grp + 1] / lrow,
-                       o[db][4 * grp + 2] / lrow, o[db][4 * grp + 3] / lrow);
+        Store4<O>::put(a.out, ob + d0, o[db][4 * grp], o[db][4 * grp + 1], o[db][4 * grp + 2],
+                       o[db][4 * grp + 3], inv);
       }
   }
 }
 
 template <typename E, typename O, int D>
 static hipError_t prefill_t(const PrefillArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL((prefill_kernel<E, O, D>), dim3(a.num_qtiles, a.num_heads, a.num_prompts), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((prefill_kernel<E, O, D>), dim3(a.per_xcd * 8), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

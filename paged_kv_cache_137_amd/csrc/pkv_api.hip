@@ -266,7 +266,7 @@ int pkv_paged_attn_prefill(const void* q, const void* k, const void* v, int32_t 
   if (out_dtype != PKV_F32 && out_dtype != dtype) return PKV_ENOTSUP;
   if (head_dim != 64 && head_dim != 128) return PKV_ENOTSUP;
   if (num_heads <= 0 || num_heads > 65535 || num_prompts < 0 || num_prompts > 65535) return PKV_EINVAL;
-  if (total_tokens < 0 || max_prompt_len < 0) return PKV_EINVAL;
+  if (total_tokens < 0 || max_prompt_len < 0 || !(scale > 0.0f) || scale > 1e30f) return PKV_EINVAL;
   if (num_prompts == 0 || max_prompt_len == 0 || total_tokens == 0) return PKV_OK;
   if (!q || !k || !v || !out || !prompt_lens) return PKV_EINVAL;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) || !aligned(prompt_lens, 4))
@@ -274,6 +274,9 @@ int pkv_paged_attn_prefill(const void* q, const void* k, const void* v, int32_t 
   if (block_tables != nullptr &&
       (max_blocks_per_seq <= 0 || (int64_t)max_blocks_per_seq * kBlock < (int64_t)max_prompt_len))
     return PKV_EINVAL;
+  const int32_t num_qtiles = (max_prompt_len + pkv::PREFILL_BLOCK_M - 1) / pkv::PREFILL_BLOCK_M;
+  const int64_t items = (int64_t)num_qtiles * num_heads * num_prompts;
+  if (items > ((int64_t)1 << 31) - 64) return PKV_EINVAL;
   int st = device_status();
   if (st != PKV_OK) return st;
   hipStream_t sm = reinterpret_cast<hipStream_t>(stream);
@@ -297,7 +300,9 @@ int pkv_paged_attn_prefill(const void* q, const void* k, const void* v, int32_t 
   a.num_prompts = num_prompts;
   a.num_heads = num_heads;
   a.max_prompt_len = max_prompt_len;
-  a.num_qtiles = (max_prompt_len + pkv::PREFILL_BLOCK_M - 1) / pkv::PREFILL_BLOCK_M;
+  a.num_qtiles = num_qtiles;
+  a.total_items = (int32_t)items;
+  a.per_xcd = (int32_t)((items + 7) / 8);
   a.scale_log2 = scale * 1.4426950408889634f;
   return launch_status(pkv::launch_prefill(a, dtype, out_dtype, head_dim, sm));
 }

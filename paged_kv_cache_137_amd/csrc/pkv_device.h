@@ -36,7 +36,13 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   u += 0x7fffu + ((u >> 16) & 1u);
   return (uint16_t)(u >> 16);
 }
+// float -> f16 bits, round to nearest even, from the float32 value as given.
+// The empty asm makes the float32 value opaque.  Without it the compiler may
+// fold a preceding multiply into a mixed-precision convert (one rounding of the
+// exact product), and a 16-bit output would then not always equal the rounding
+// of the float32 output.
 __device__ __forceinline__ uint16_t f32_to_f16_bits(float f) {
+  asm volatile("" : "+v"(f));
   return __builtin_bit_cast(uint16_t, (_Float16)f);
 }
 

@@ -54,6 +54,8 @@ struct PrefillArgs {
   int32_t num_heads;
   int32_t max_prompt_len;
   int32_t num_qtiles;
+  int32_t total_items;  // num_qtiles * num_heads * num_prompts
+  int32_t per_xcd;      // ceil(total_items / 8): work items per XCD slice of the grid
   float scale_log2;
 };
 
