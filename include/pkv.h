@@ -211,6 +211,27 @@ int pkv_paged_attn_prefill(const void* q, const void* k, const void* v, int32_t 
                            const int32_t* prompt_lens, int32_t num_prompts, int64_t total_tokens,
                            int32_t max_prompt_len, float scale, void* out, int32_t out_dtype, void* stream);
 
+/*
+ * pkv_copy_blocks - copy whole physical blocks, for copy-on-write.
+ *
+ * When a sequence must write into a block it shares with others, the block is
+ * copied first and the writer's table entry moves to the copy ("vLLM &
+ * PagedAttention ...", section VII, Figure 8).  All such copies of a step are
+ * batched into one kernel launch, instead of one small memory copy each
+ * (section X, third kernel detail).
+ *
+ *   k_cache, v_cache  the pool (layout above), modified in place
+ *   block_pairs   int64 [num_pairs][2] = (source block, destination block)
+ * For every pair and every head:
+ *   cache[dst][h][:][:] = cache[src][h][:][:]      (keys and values, byte-exact)
+ * Pairs with an id outside [0, num_blocks) are skipped.  Destinations must be
+ * distinct and must not also be sources in the same call; otherwise, which
+ * bytes land is unspecified.  PKV_VALIDATE=1 checks this.  num_pairs == 0 is a
+ * no-op.
+ */
+int pkv_copy_blocks(void* k_cache, void* v_cache, const pkv_cache_desc* desc, const int64_t* block_pairs,
+                    int64_t num_pairs, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -64,6 +64,26 @@ def cache_write(k_cache, v_cache, k, v, slot_mapping, block_size: int):
     return kc, vc
 
 
+def copy_blocks(k_cache, v_cache, block_pairs):
+    """Copy whole physical blocks (all heads, keys and values).  Returns new pool arrays.
+
+    For each (src, dst) pair, cache[dst] = cache[src], byte for byte.  This is the
+    copy-on-write step: a write into a shared block copies the block first, and
+    the writer moves to the copy (P3 section VII, Figure 8).  All copies of a step
+    are batched into one launch (P3 section X).  Pairs are applied in order.
+    """
+    kc, vc = k_cache.copy(), v_cache.copy()
+    ut = _UINT[kc.dtype.itemsize]
+    kcu, vcu = kc.view(ut), vc.view(ut)
+    nb = kc.shape[0]
+    for src, dst in np.asarray(block_pairs, dtype=np.int64).reshape(-1, 2):
+        if not (0 <= src < nb and 0 <= dst < nb):
+            raise IndexError(f"block pair ({src}, {dst}) outside a pool of {nb} blocks")
+        kcu[dst] = kcu[src]
+        vcu[dst] = vcu[src]
+    return kc, vc
+
+
 def gather(cache: np.ndarray, block_table, context_len: int, block_size: int) -> np.ndarray:
     """A sequence's contiguous [num_heads][context_len][head_dim] view, built block by block.
 

@@ -87,6 +87,8 @@ class BlockManager:
 
         When the last block is shared, it is copied first: the (source,
         destination) pair is queued in pending_copies for the device-side copy.
+        A step applies take_copies() (pkv_copy_blocks) before it writes the
+        step's new tokens, so every copy sees the block as it was before the step.
         """
         table = self.tables[seq]
         pos = self.lens[seq]

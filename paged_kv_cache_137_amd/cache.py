@@ -48,5 +48,9 @@ class PagedKVCache:
         """Write new tokens' keys and values into the physical blocks."""
         ops.kv_cache_write(k, v, slot_mapping, self.k_cache, self.v_cache)
 
+    def copy_blocks(self, block_pairs: torch.Tensor) -> None:
+        """Copy-on-write: copy whole blocks, (src, dst) pairs, keys and values, in one launch."""
+        ops.copy_blocks(self.k_cache, self.v_cache, block_pairs)
+
     def paged_attn_decode(self, q, block_tables, context_lens, scale, out, **kw):
         return ops.paged_attn_decode(q, self.k_cache, self.v_cache, block_tables, context_lens, scale, out, **kw)

@@ -47,6 +47,9 @@ namespace pkv {
 #ifndef PKV_DEC_NT
 #define PKV_DEC_NT 1
 #endif
+#ifndef PKV_DEC_PP
+#define PKV_DEC_PP 1
+#endif
 
 constexpr int BS = 16;             // tokens per block
 constexpr int NW = PKV_DEC_NW;     // wavefronts per workgroup
@@ -95,15 +98,31 @@ __global__ __launch_bounds__(1024) void decode_plan_kernel(const DecodeArgs a) {
     }
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    int run = 0;
-    for (int b = PLAN_BUCKETS - 1; b >= 0; --b) {
-      const int c = cnt[b];
-      cnt[b] = run;
-      run += c;
+  // Exclusive scan of the bucket counts in descending bucket order: thread i
+  // (i < PLAN_BUCKETS) owns bucket PLAN_BUCKETS-1-i.  Wave-level inclusive scans
+  // with shuffles, then the earlier waves' totals are added.
+  {
+    __shared__ int wave_tot[(PLAN_BUCKETS + 63) / 64];
+    const int i = threadIdx.x;
+    const int lane = i & 63, wv = i >> 6;
+    const int b = PLAN_BUCKETS - 1 - i;
+    const int mine = i < PLAN_BUCKETS ? cnt[b] : 0;
+    int incl = mine;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int y = __shfl_up(incl, d, 64);
+      if (lane >= d) incl += y;
     }
-    a.work_ctrl[0] = 0;
-    a.work_ctrl[1] = run;
+    if (i < PLAN_BUCKETS && lane == 63) wave_tot[wv] = incl;
+    if (i == PLAN_BUCKETS - 1 && lane != 63) wave_tot[wv] = incl;
+    __syncthreads();
+    int before = 0;
+    for (int k = 0; k < wv && k < (PLAN_BUCKETS + 63) / 64; ++k) before += wave_tot[k];
+    if (i < PLAN_BUCKETS) cnt[b] = before + incl - mine;
+    if (i == PLAN_BUCKETS - 1) {
+      a.work_ctrl[0] = 0;
+      a.work_ctrl[1] = before + incl;
+    }
   }
   __syncthreads();
   for (int s = threadIdx.x; s < a.num_seqs; s += blockDim.x) {
@@ -231,6 +250,7 @@ __global__ __launch_bounds__(NW * 64) void decode_partial_kernel(const DecodeArg
       };
       int j = w;
       if (j >= cn) continue;
+#if PKV_DEC_PP
       uint4 kA[NI], vA[NI], kB[NI], vB[NI];
       bool badA, badB;
       load(phys_of(j, badA), kA, vA);
@@ -248,6 +268,14 @@ __global__ __launch_bounds__(NW * 64) void decode_partial_kernel(const DecodeArg
       } else {
         consume(kA, vA, cb + j, badA);
       }
+#else
+      for (; j < cn; j += NW) {
+        uint4 kA[NI], vA[NI];
+        bool badA;
+        load(phys_of(j, badA), kA, vA);
+        consume(kA, vA, cb + j, badA);
+      }
+#endif
     }
 
     // Merge the ROWS running states of this unit: max, rescaled sums.

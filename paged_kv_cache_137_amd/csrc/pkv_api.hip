@@ -307,4 +307,43 @@ int pkv_paged_attn_prefill(const void* q, const void* k, const void* v, int32_t 
   return launch_status(pkv::launch_prefill(a, dtype, out_dtype, head_dim, sm));
 }
 
+int pkv_copy_blocks(void* k_cache, void* v_cache, const pkv_cache_desc* desc, const int64_t* block_pairs,
+                    int64_t num_pairs, void* stream) {
+  int st = check_desc(desc);
+  if (st != PKV_OK) return st;
+  if (num_pairs < 0) return PKV_EINVAL;
+  if (num_pairs == 0) return PKV_OK;
+  if (!k_cache || !v_cache || !block_pairs) return PKV_EINVAL;
+  if (!aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(block_pairs, 8)) return PKV_EINVAL;
+  if (desc->num_heads > 65535) return PKV_EINVAL;
+  st = device_status();
+  if (st != PKV_OK) return st;
+  hipStream_t sm = reinterpret_cast<hipStream_t>(stream);
+  if (validate_mode()) {
+    std::vector<int64_t> pairs;
+    if (!copy_to_host(pairs, block_pairs, (size_t)num_pairs * 2, sm)) return PKV_EDEVICE;
+    std::vector<int64_t> dsts, srcs;
+    for (int64_t i = 0; i < num_pairs; ++i) {
+      const int64_t s0 = pairs[2 * i], d0 = pairs[2 * i + 1];
+      if (s0 < 0 || s0 >= desc->num_blocks || d0 < 0 || d0 >= desc->num_blocks) return PKV_EINVAL;
+      srcs.push_back(s0);
+      dsts.push_back(d0);
+    }
+    std::sort(dsts.begin(), dsts.end());
+    std::sort(srcs.begin(), srcs.end());
+    if (std::adjacent_find(dsts.begin(), dsts.end()) != dsts.end()) return PKV_EINVAL;
+    for (int64_t d0 : dsts)
+      if (std::binary_search(srcs.begin(), srcs.end(), d0)) return PKV_EINVAL;
+  }
+  pkv::CopyArgs a{};
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.pairs = block_pairs;
+  a.num_pairs = num_pairs;
+  a.num_blocks = desc->num_blocks;
+  a.num_heads = desc->num_heads;
+  a.tile_bytes = desc->block_size * desc->head_dim * (desc->dtype == PKV_F32 ? 4 : 2);
+  return launch_status(pkv::launch_copy_blocks(a, sm));
+}
+
 }  // extern "C"

@@ -59,7 +59,18 @@ struct PrefillArgs {
   float scale_log2;
 };
 
+struct CopyArgs {
+  void* k_cache;
+  void* v_cache;
+  const int64_t* pairs;  // [num_pairs][2] (src, dst)
+  int64_t num_pairs;
+  int64_t num_blocks;
+  int32_t num_heads;
+  int32_t tile_bytes;  // block_size * head_dim * element bytes
+};
+
 // Each returns a hipError_t from the launch.
+hipError_t launch_copy_blocks(const CopyArgs& a, hipStream_t stream);
 hipError_t launch_kv_cache_write(const WriteArgs& a, hipStream_t stream);
 hipError_t launch_decode_partial(const DecodeArgs& a, int dtype, int out_dtype, int head_dim, hipStream_t stream);
 hipError_t launch_decode_reduce(const DecodeArgs& a, int out_dtype, int head_dim, hipStream_t stream);

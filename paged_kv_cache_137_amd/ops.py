@@ -76,6 +76,20 @@ def kv_cache_write(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor,
             _ptr(k), _ptr(v), _ptr(slot_mapping), T, _ptr(k_cache), _ptr(v_cache), ctypes.byref(desc), _stream(dev)))
 
 
+def copy_blocks(k_cache: torch.Tensor, v_cache: torch.Tensor, block_pairs: torch.Tensor) -> None:
+    """Copy whole blocks, (src, dst) rows of int64 block_pairs [n][2], keys and values, in one launch."""
+    _need(k_cache, "k_cache", dim=4)
+    dev = k_cache.device
+    _need(v_cache, "v_cache", dtype=k_cache.dtype, device=dev)
+    _need(block_pairs, "block_pairs", dtype=torch.int64, dim=2, device=dev)
+    if v_cache.shape != k_cache.shape or block_pairs.shape[1] != 2:
+        raise ValueError("block_pairs must be [n][2]; k_cache and v_cache must match")
+    desc = cache_desc(k_cache)
+    with torch.cuda.device(dev):
+        check("pkv_copy_blocks", lib().pkv_copy_blocks(
+            _ptr(k_cache), _ptr(v_cache), ctypes.byref(desc), _ptr(block_pairs), block_pairs.shape[0], _stream(dev)))
+
+
 def decode_workspace_bytes(num_seqs: int, num_heads: int, head_dim: int, max_context_len: int,
                            partition_size: int = DEFAULT_PARTITION) -> int:
     return int(lib().pkv_decode_workspace_bytes(num_seqs, num_heads, head_dim, max_context_len, partition_size))

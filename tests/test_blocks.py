@@ -115,3 +115,37 @@ def test_sharing_config_accounting():
     used = d.num_blocks - m.num_free
     assert used == d.info["physical_blocks_used"]
     assert m.context_lens(range(d.num_seqs)).tolist() == d.context_lens.tolist()
+
+
+def test_figure9_beam_prune_and_regrow():
+    # P3 section VII, Figure 9 prints only the block ids: all four candidates
+    # share prompt block 0; pruning frees 2, 4, 5 and 8; survivors get 9-12.  This
+    # history (block size 4, free list in increasing order) is one tree that is
+    # consistent with those ids.
+    g = GOLD["figure9"]
+    B = 4
+    m = PB.BlockManager(16, B)
+    m.add_sequence(0, B)                      # the prompt fills block 0
+    for c in (1, 2, 3):
+        m.fork(0, c)
+    assert m.ref[g["prompt_block"]] == g["beam_width"]
+    for c in range(4):                        # level 1: candidates take blocks 1, 2, 3, 4
+        for _ in range(B):
+            m.append_token(c)
+    for c in (1, 0, 2, 3):                    # level 2, in this order: blocks 5, 6, 7, 8
+        for _ in range(B):
+            m.append_token(c)
+    assert [m.tables[c][1:] for c in range(4)] == [[1, 6], [2, 5], [3, 7], [4, 8]]
+    before = set(m._free)
+    m.free(1)                                 # prune candidates 1 and 3
+    m.free(3)
+    freed = sorted(set(m._free) - before)
+    assert freed == g["freed_blocks"]
+    assert all(m.ref[b] == 0 for b in freed)
+    assert m.ref[g["prompt_block"]] == 2
+    m.fork(0, 4)                              # survivors branch back to four candidates
+    m.fork(2, 5)
+    new = [m.append_token(c) // B for c in (0, 4, 2, 5)]  # each starts a fresh block
+    assert new == g["new_blocks"]
+    assert m.take_copies() == []              # full shared blocks are never copied
+    assert m.ref[1] == 2 and m.ref[6] == 2 and m.ref[3] == 2 and m.ref[7] == 2

@@ -417,3 +417,18 @@ def test_planted_mistake_is_caught(name, monkeypatch):
 
 def test_unmutated_oracle_passes_all_pins():
     assert _all_pins_pass(A.paged_decode, A.causal_prefill)
+
+
+def test_copy_blocks_duplicates_whole_blocks_only():
+    rng = np.random.default_rng(12)
+    kc = rng.standard_normal((6, 2, 4, 3)).astype(np.float16)
+    vc = rng.standard_normal((6, 2, 4, 3)).astype(np.float16)
+    nk, nv = A.copy_blocks(kc, vc, [(1, 4), (2, 5)])
+    assert np.array_equal(nk[4].view(np.uint16), kc[1].view(np.uint16))
+    assert np.array_equal(nv[5].view(np.uint16), vc[2].view(np.uint16))
+    for b in (0, 1, 2, 3):
+        assert np.array_equal(nk[b].view(np.uint16), kc[b].view(np.uint16))
+    # A table pointing at the copy gathers what the original gathers.
+    assert np.array_equal(A.gather(nk, [4, 0], 7, 4), A.gather(kc, [1, 0], 7, 4))
+    with pytest.raises(IndexError):
+        A.copy_blocks(kc, vc, [(0, 6)])
