@@ -196,10 +196,11 @@ int pkv_paged_attn_decode_reduce(const void* q, const void* k_cache, const void*
  *   q, k, v        packed prompts [total_tokens][num_heads][head_dim] of `dtype`
  *                  (PKV_F16 or PKV_BF16).  Prompt p occupies rows
  *                  off_p .. off_p + prompt_lens[p] - 1, off_p = sum of earlier lengths.
- *   block_tables   int32 [num_prompts][max_blocks_per_seq] or NULL.  Reserved.
- *                  Prefill attends over the contiguous k, v above.  After
+ *   block_tables   int32 [num_prompts][max_blocks_per_seq] or NULL.  Unused here:
+ *                  prefill attends over the contiguous k, v above.  After
  *                  pkv_kv_cache_write those hold the same bytes as the
  *                  prompt's blocks, so the result is the same either way.
+ *                  pkv_paged_attn_prefill_cached reads through the table.
  *   prompt_lens    int32 [num_prompts], each in [0, max_prompt_len]; their sum
  *                  must equal total_tokens.  Rows beyond total_tokens are never
  *                  touched.
@@ -210,6 +211,39 @@ int pkv_paged_attn_prefill(const void* q, const void* k, const void* v, int32_t 
                            int32_t dtype, const int32_t* block_tables, int32_t max_blocks_per_seq,
                            const int32_t* prompt_lens, int32_t num_prompts, int64_t total_tokens,
                            int32_t max_prompt_len, float scale, void* out, int32_t out_dtype, void* stream);
+
+/*
+ * pkv_paged_attn_prefill_cached - prompt phase over a cached prefix, through the pool.
+ *
+ * A request whose first tokens are a shared prefix already in the cache (a
+ * system prompt, few-shot examples) maps those logical blocks onto the cached
+ * physical blocks.  It then runs the prompt phase only over its own new
+ * tokens ("vLLM & PagedAttention ...", section VII, shared prefix).  New token i
+ * of prompt p sits at position prefix_lens[p] + i.  It attends causally to
+ * positions 0 .. prefix_lens[p] + i, all read through the prompt's block table
+ * (section I attention equation; section III block-wise evaluation).  The new
+ * tokens' K/V must already be in the pool (pkv_kv_cache_write), as in a mixed
+ * step: new KV is written, then read through the tables (section V).
+ *
+ *   q             [total_tokens][num_heads][head_dim] of desc->dtype (PKV_F16 or PKV_BF16):
+ *                 the new tokens only, packed prompt after prompt
+ *   k_cache, v_cache, desc  the pool (read only)
+ *   block_tables  int32 [num_prompts][max_blocks_per_seq]; row p covers positions
+ *                 0 .. prefix_lens[p] + prompt_lens[p] - 1
+ *   prefix_lens   int32 [num_prompts], each in [0, max_prefix_len], or NULL for no prefix
+ *   prompt_lens   int32 [num_prompts], each in [0, max_prompt_len], summing to total_tokens
+ *   max_prefix_len + max_prompt_len <= max_blocks_per_seq * block_size
+ *   scale         positive and finite
+ *   out           [total_tokens][num_heads][head_dim] of out_dtype (PKV_F32 or desc->dtype)
+ * With every prefix length 0 this is causal prefill reading K/V through the
+ * table: the same result as pkv_paged_attn_prefill over the same bytes.  A
+ * table entry outside the pool makes the affected outputs NaN.
+ */
+int pkv_paged_attn_prefill_cached(const void* q, const void* k_cache, const void* v_cache, const pkv_cache_desc* desc,
+                                  const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* prefix_lens,
+                                  const int32_t* prompt_lens, int32_t num_prompts, int64_t total_tokens,
+                                  int32_t max_prompt_len, int32_t max_prefix_len, float scale, void* out,
+                                  int32_t out_dtype, void* stream);
 
 /*
  * pkv_copy_blocks - copy whole physical blocks, for copy-on-write.

@@ -151,3 +151,32 @@ def causal_prefill(q, k, v, prompt_lens, scale: float, dtype: str, prompts=None)
             p_ = np.exp(z)
             out[a:b, h, :] = (p_ @ V[:, h, :]) / p_.sum(axis=1, keepdims=True)
     return out
+
+
+def prefix_prefill(q, k_cache, v_cache, block_tables, prefix_lens, prompt_lens, scale: float, dtype: str,
+                   block_size: int = 16, prompts=None) -> np.ndarray:
+    """Prompt-phase attention of new tokens over a cached prefix plus themselves; float64 [T][H][D].
+
+    Prompt p already has prefix_lens[p] tokens in the pool (the cached shared
+    prefix of P3 section VII), followed by its prompt_lens[p] new tokens, whose
+    K/V are in the pool too.  All of them are read through the prompt's block
+    table.  New token i sits at position prefix_lens[p] + i.  It attends to
+    positions 0 .. prefix_lens[p] + i, the t <= i limit of P3 section I's
+    equation.  Compute runs only over the new tokens.  q and the output hold the
+    new tokens only, packed prompt after prompt.
+    """
+    T, H, D = q.shape
+    out = np.full((T, H, D), np.nan)
+    offs = np.concatenate([[0], np.cumsum(np.asarray(prompt_lens, dtype=np.int64))])
+    for p in (range(len(prompt_lens)) if prompts is None else prompts):
+        C, L = int(prefix_lens[p]), int(prompt_lens[p])
+        if L == 0:
+            continue
+        K = to_f64(gather(k_cache, block_tables[p], C + L, block_size), dtype)
+        V = to_f64(gather(v_cache, block_tables[p], C + L, block_size), dtype)
+        Q = to_f64(q[offs[p] : offs[p + 1]], dtype)
+        for i in range(L):
+            n = C + i + 1
+            for h in range(H):
+                out[offs[p] + i, h] = attend(Q[i, h], K[h, :n], V[h, :n], scale)
+    return out

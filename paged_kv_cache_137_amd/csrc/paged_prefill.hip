@@ -38,6 +38,12 @@
 //    straddle the diagonal or the prompt end are masked by selecting -inf.
 //  - Query tiles are dispatched longest-first (descending tile index), to even
 //    out the causal triangle's load.
+//  - Cached-prefix variant: keys and values are gathered from the paged pool
+//    through the prompt's block table.  Each 16-key run is one contiguous
+//    (block, head) tile.  Positions before the prompt's new tokens are a
+//    shared prefix that is already cached ("vLLM & PagedAttention ...",
+//    section VII: the prompt phase runs only over the request's own input).
+//    The causal limit is then shifted by the prefix length.
 #include <type_traits>
 
 #include "pkv_device.h"
@@ -115,8 +121,15 @@ template <> struct Store4<f16_t> {
   }
 };
 
-template <typename E, typename O, int D>
+// PAGED = false: keys/values are the prompt's own packed rows (a fresh prompt).
+// PAGED = true:  keys/values are read from the pool through the prompt's block
+//                table.  The first prefix_lens[p] positions are a cached prefix;
+//                the prompt's new tokens follow (their K/V already written).
+template <typename E, typename O, int D, bool PAGED>
 __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
+  // Two quiet NaNs of the element type, packed: the value of a tile whose
+  // block id lies outside the pool.
+  constexpr uint32_t E16_NAN2 = std::is_same<E, bf16_t>::value ? 0x7fc07fc0u : 0x7e007e00u;
   constexpr int BM = PREFILL_BLOCK_M;      // query rows per workgroup (4 waves x 32)
   constexpr int BN = 64;                   // keys per LDS tile
   constexpr int KS = D / 16;               // k-steps of Q K^T
@@ -158,6 +171,16 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
 #pragma unroll
   for (int sft = 32; sft >= 1; sft >>= 1) off += __shfl_xor(off, sft, 64);
   if (off + L > a.total_tokens) L = (int)max(0ll, (long long)a.total_tokens - off);
+  // C: cached prefix tokens ahead of the new ones; keys are indexed by absolute
+  // position 0 .. C+L-1, and new token i sits at position C + i.
+  int C = 0;
+  const int32_t* trow = nullptr;
+  if constexpr (PAGED) {
+    const int cap = a.max_blocks_per_seq * 16;
+    C = a.prefix_lens != nullptr ? min(max(a.prefix_lens[pr], 0), cap) : 0;
+    L = min(L, cap - C);
+    trow = a.block_tables + (int64_t)pr * a.max_blocks_per_seq;
+  }
   if (L <= m0) return;
 
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -185,15 +208,15 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
 
   // Per-thread staging slots (fixed for the whole loop): K chunk i is row
   // krow[i], chunk kch[i] of the tile; the V group is keys 4*vg..+3, dims vch*8..+7.
-  int krow[KCH];
+  int krow[KCH], kch[KCH];
   uint32_t koff[KCH], klds[KCH];
 #pragma unroll
   for (int i = 0; i < KCH; ++i) {
     const int idx = threadIdx.x + i * 256;
     krow[i] = idx / (D / 8);
-    const int ch = idx % (D / 8);
-    koff[i] = krow[i] * rsb + ch * 16;
-    klds[i] = krow[i] * KROW + ch * 16;
+    kch[i] = idx % (D / 8);
+    koff[i] = krow[i] * rsb + kch[i] * 16;
+    klds[i] = krow[i] * KROW + kch[i] * 16;
   }
   const int vg = threadIdx.x % (BN / 4), vch = threadIdx.x / (BN / 4);
   const uint32_t voff = 4 * vg * rsb + vch * 16;
@@ -209,16 +232,35 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
   auto gload = [&](Stage& st_, int n0) {
     uint4 (&kst)[KCH] = st_.k;
     uint4 (&vst)[4] = st_.v;
-    const char* kt = kb + (int64_t)n0 * rsb;
-    const char* vt = vb + (int64_t)n0 * rsb;
+    if constexpr (PAGED) {
+      // Key position -> (physical block from the table, offset in the block).
+      // An id outside the pool yields NaN, so the result shows it.
+      const uint4 nanv = make_uint4(E16_NAN2, E16_NAN2, E16_NAN2, E16_NAN2);
+      auto fetch = [&](const void* pool, int key, int ch) -> uint4 {
+        if (key >= C + L) return make_uint4(0u, 0u, 0u, 0u);
+        const int ph = trow[key >> 4];
+        if ((uint64_t)(uint32_t)ph >= (uint64_t)a.num_blocks) return nanv;
+        const int64_t row = ((int64_t)ph * a.num_heads + h) * 16 + (key & 15);
+        return *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(pool) + row * (D * 2) + ch * 16);
+      };
 #pragma unroll
-    for (int i = 0; i < KCH; ++i)
-      kst[i] = n0 + krow[i] < L ? *reinterpret_cast<const uint4*>(kt + koff[i]) : make_uint4(0u, 0u, 0u, 0u);
-    if (threadIdx.x < VG) {
+      for (int i = 0; i < KCH; ++i) kst[i] = fetch(a.k_cache, n0 + krow[i], kch[i]);
+      if (threadIdx.x < VG) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        vst[i] = n0 + 4 * vg + i < L ? *reinterpret_cast<const uint4*>(vt + voff + i * rsb)
-                                     : make_uint4(0u, 0u, 0u, 0u);
+        for (int i = 0; i < 4; ++i) vst[i] = fetch(a.v_cache, n0 + 4 * vg + i, vch);
+      }
+    } else {
+      const char* kt = kb + (int64_t)n0 * rsb;
+      const char* vt = vb + (int64_t)n0 * rsb;
+#pragma unroll
+      for (int i = 0; i < KCH; ++i)
+        kst[i] = n0 + krow[i] < L ? *reinterpret_cast<const uint4*>(kt + koff[i]) : make_uint4(0u, 0u, 0u, 0u);
+      if (threadIdx.x < VG) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          vst[i] = n0 + 4 * vg + i < L ? *reinterpret_cast<const uint4*>(vt + voff + i * rsb)
+                                       : make_uint4(0u, 0u, 0u, 0u);
+      }
     }
   };
   // K row-major [key][dim]; V transposed to [dim][key], 4 keys per 8-byte store.
@@ -252,10 +294,10 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
 #pragma unroll
     for (int j = 0; j < 16; ++j) o[db][j] = 0.f;
   float mrow = NEG_BIG, lrow = 0.f;
-  const int lim = min(qi, L - 1);  // last key this query may see
+  const int lim = C + min(qi, L - 1);  // last key position this query may see
 
-  const int kend = min(L, m0 + BM);     // keys any query of the workgroup sees
-  const int wkend = min(L, qrow0 + 32); // keys any query of this wave sees
+  const int kend = C + min(L, m0 + BM);     // keys any query of the workgroup sees
+  const int wkend = C + min(L, qrow0 + 32); // keys any query of this wave sees
 
   // One 64-key tile from LDS buffer `buf`, starting at key n0, as NSUB (1 or 2)
   // sub-tiles of 32 keys.  The sub-tiles' score chains are independent, so
@@ -281,7 +323,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
         st[u] = mfma32<E>(*reinterpret_cast<const uint4*>(kr + kk * 32), qf[kk], st[u]);
       }
 
-    if ((n0 + 32 * NSUB - 1 > qrow0) || (n0 + 32 * NSUB > L)) {  // straddles the diagonal or the prompt end
+    if ((n0 + 32 * NSUB - 1 > C + qrow0) || (n0 + 32 * NSUB > C + L)) {  // straddles the diagonal or the end
 #pragma unroll
       for (int u = 0; u < NSUB; ++u) {
         const int room = lim - (n0 + 32 * u + 4 * hf);  // element j is visible iff its offset <= room
@@ -365,21 +407,26 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
   }
 }
 
-template <typename E, typename O, int D>
+template <typename E, typename O, int D, bool PAGED>
 static hipError_t prefill_t(const PrefillArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL((prefill_kernel<E, O, D>), dim3(a.per_xcd * 8), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((prefill_kernel<E, O, D, PAGED>), dim3(a.per_xcd * 8), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
-template <typename E>
+template <typename E, bool PAGED>
 static hipError_t prefill_d(const PrefillArgs& a, int out_dtype, int head_dim, hipStream_t st) {
-  if (head_dim == 128) return out_dtype == 0 ? prefill_t<E, f32_t, 128>(a, st) : prefill_t<E, E, 128>(a, st);
-  return out_dtype == 0 ? prefill_t<E, f32_t, 64>(a, st) : prefill_t<E, E, 64>(a, st);
+  if (head_dim == 128)
+    return out_dtype == 0 ? prefill_t<E, f32_t, 128, PAGED>(a, st) : prefill_t<E, E, 128, PAGED>(a, st);
+  return out_dtype == 0 ? prefill_t<E, f32_t, 64, PAGED>(a, st) : prefill_t<E, E, 64, PAGED>(a, st);
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, int dtype, int out_dtype, int head_dim, hipStream_t st) {
-  if (dtype == 1) return prefill_d<f16_t>(a, out_dtype, head_dim, st);
-  return prefill_d<bf16_t>(a, out_dtype, head_dim, st);
+  if (a.k_cache != nullptr) {
+    if (dtype == 1) return prefill_d<f16_t, true>(a, out_dtype, head_dim, st);
+    return prefill_d<bf16_t, true>(a, out_dtype, head_dim, st);
+  }
+  if (dtype == 1) return prefill_d<f16_t, false>(a, out_dtype, head_dim, st);
+  return prefill_d<bf16_t, false>(a, out_dtype, head_dim, st);
 }
 
 }  // namespace pkv

@@ -307,6 +307,70 @@ int pkv_paged_attn_prefill(const void* q, const void* k, const void* v, int32_t 
   return launch_status(pkv::launch_prefill(a, dtype, out_dtype, head_dim, sm));
 }
 
+int pkv_paged_attn_prefill_cached(const void* q, const void* k_cache, const void* v_cache, const pkv_cache_desc* desc,
+                                  const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* prefix_lens,
+                                  const int32_t* prompt_lens, int32_t num_prompts, int64_t total_tokens,
+                                  int32_t max_prompt_len, int32_t max_prefix_len, float scale, void* out,
+                                  int32_t out_dtype, void* stream) {
+  int st = check_desc(desc);
+  if (st != PKV_OK) return st;
+  if (desc->dtype != PKV_F16 && desc->dtype != PKV_BF16) return PKV_ENOTSUP;
+  if (out_dtype != PKV_F32 && out_dtype != desc->dtype) return PKV_ENOTSUP;
+  if (desc->num_heads > 65535 || num_prompts < 0 || num_prompts > 65535) return PKV_EINVAL;
+  if (total_tokens < 0 || max_prompt_len < 0 || max_prefix_len < 0 || !(scale > 0.0f) || scale > 1e30f)
+    return PKV_EINVAL;
+  if (num_prompts == 0 || max_prompt_len == 0 || total_tokens == 0) return PKV_OK;
+  if (!q || !k_cache || !v_cache || !out || !prompt_lens || !block_tables) return PKV_EINVAL;
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16) ||
+      !aligned(prompt_lens, 4) || !aligned(block_tables, 4) || !aligned(prefix_lens, 4))
+    return PKV_EINVAL;
+  if (max_blocks_per_seq <= 0 ||
+      (int64_t)max_blocks_per_seq * kBlock < (int64_t)max_prompt_len + (int64_t)max_prefix_len)
+    return PKV_EINVAL;
+  const int32_t num_qtiles = (max_prompt_len + pkv::PREFILL_BLOCK_M - 1) / pkv::PREFILL_BLOCK_M;
+  const int64_t items = (int64_t)num_qtiles * desc->num_heads * num_prompts;
+  if (items > ((int64_t)1 << 31) - 64) return PKV_EINVAL;
+  st = device_status();
+  if (st != PKV_OK) return st;
+  hipStream_t sm = reinterpret_cast<hipStream_t>(stream);
+  if (validate_mode()) {
+    std::vector<int32_t> lens, pre, tab;
+    if (!copy_to_host(lens, prompt_lens, (size_t)num_prompts, sm)) return PKV_EDEVICE;
+    if (prefix_lens != nullptr && !copy_to_host(pre, prefix_lens, (size_t)num_prompts, sm)) return PKV_EDEVICE;
+    if (!copy_to_host(tab, block_tables, (size_t)num_prompts * max_blocks_per_seq, sm)) return PKV_EDEVICE;
+    int64_t sum = 0;
+    for (int32_t p = 0; p < num_prompts; ++p) {
+      const int32_t L = lens[p], C = prefix_lens ? pre[p] : 0;
+      if (L < 0 || L > max_prompt_len || C < 0 || C > max_prefix_len) return PKV_EINVAL;
+      sum += L;
+      for (int32_t j = 0; j < (C + L + kBlock - 1) / kBlock; ++j) {
+        const int32_t b = tab[(size_t)p * max_blocks_per_seq + j];
+        if (b < 0 || b >= desc->num_blocks) return PKV_EINVAL;
+      }
+    }
+    if (sum != total_tokens) return PKV_EINVAL;
+  }
+  pkv::PrefillArgs a{};
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.prefix_lens = prefix_lens;
+  a.num_blocks = desc->num_blocks;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.prompt_lens = prompt_lens;
+  a.out = out;
+  a.total_tokens = total_tokens;
+  a.num_prompts = num_prompts;
+  a.num_heads = desc->num_heads;
+  a.max_prompt_len = max_prompt_len;
+  a.num_qtiles = num_qtiles;
+  a.total_items = (int32_t)items;
+  a.per_xcd = (int32_t)((items + 7) / 8);
+  a.scale_log2 = scale * 1.4426950408889634f;
+  return launch_status(pkv::launch_prefill(a, desc->dtype, out_dtype, desc->head_dim, sm));
+}
+
 int pkv_copy_blocks(void* k_cache, void* v_cache, const pkv_cache_desc* desc, const int64_t* block_pairs,
                     int64_t num_pairs, void* stream) {
   int st = check_desc(desc);

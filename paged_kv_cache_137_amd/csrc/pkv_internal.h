@@ -47,6 +47,14 @@ struct PrefillArgs {
   const void* q;
   const void* k;
   const void* v;
+  // Cached-prefix form: K/V come from the pool through the block tables instead
+  // of k/v (k_cache != nullptr selects it).
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_tables;
+  const int32_t* prefix_lens;  // may be null: no prefix
+  int64_t num_blocks;
+  int32_t max_blocks_per_seq;
   const int32_t* prompt_lens;
   void* out;
   int64_t total_tokens;

@@ -191,3 +191,47 @@ def paged_attn_prefill(q, k, v, block_tables, prompt_lens, out, *, scale: float 
             prompt_lens.shape[0], T, int(max_prompt_len), float(scale), _ptr(out), pkv_dtype(out.dtype),
             _stream(dev)))
     return out
+
+
+def paged_attn_prefill_cached(q, k_cache, v_cache, block_tables, prefix_lens, prompt_lens, out, *,
+                              scale: float | None = None, max_prompt_len: int | None = None,
+                              max_prefix_len: int | None = None):
+    """Prompt phase of new tokens q [T][H][D] over cached prefixes plus themselves; fills out.
+
+    Prompt p's first prefix_lens[p] positions are already cached, and its new
+    tokens' K/V have been written after them.  Everything is read through
+    block_tables.  prefix_lens may be None (no prefix).  max_prompt_len and
+    max_prefix_len bound the entries; by default they are T and the table
+    capacity minus max_prompt_len.
+    """
+    _need(k_cache, "k_cache", dim=4)
+    dev = k_cache.device
+    _need(v_cache, "v_cache", dtype=k_cache.dtype, device=dev)
+    _need(q, "q", dtype=k_cache.dtype, dim=3, device=dev)
+    _need(block_tables, "block_tables", dtype=torch.int32, dim=2, device=dev)
+    _need(prompt_lens, "prompt_lens", dtype=torch.int32, dim=1, device=dev)
+    if prefix_lens is not None:
+        _need(prefix_lens, "prefix_lens", dtype=torch.int32, dim=1, device=dev)
+    _need(out, "out", dim=3, device=dev)
+    T, H, D = q.shape
+    if out.shape != q.shape or out.dtype not in (torch.float32, q.dtype):
+        raise ValueError("out must be [T][H][D] of float32 or q's dtype")
+    if v_cache.shape != k_cache.shape or (H, D) != (k_cache.shape[1], k_cache.shape[3]):
+        raise ValueError("q [T][H][D] does not match the cache")
+    P = prompt_lens.shape[0]
+    if block_tables.shape[0] != P or (prefix_lens is not None and prefix_lens.shape[0] != P):
+        raise ValueError("one block table row and one prefix length per prompt")
+    mbps = block_tables.shape[1]
+    if max_prompt_len is None:
+        max_prompt_len = T
+    if max_prefix_len is None:
+        max_prefix_len = max(0, mbps * k_cache.shape[2] - max_prompt_len)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    desc = cache_desc(k_cache)
+    with torch.cuda.device(dev):
+        check("pkv_paged_attn_prefill_cached", lib().pkv_paged_attn_prefill_cached(
+            _ptr(q), _ptr(k_cache), _ptr(v_cache), ctypes.byref(desc), _ptr(block_tables), mbps,
+            _ptr(prefix_lens), _ptr(prompt_lens), P, T, int(max_prompt_len), int(max_prefix_len), float(scale),
+            _ptr(out), pkv_dtype(out.dtype), _stream(dev)))
+    return out

@@ -432,3 +432,32 @@ def test_copy_blocks_duplicates_whole_blocks_only():
     assert np.array_equal(A.gather(nk, [4, 0], 7, 4), A.gather(kc, [1, 0], 7, 4))
     with pytest.raises(IndexError):
         A.copy_blocks(kc, vc, [(0, 6)])
+
+
+def test_prefix_prefill_reduces_to_causal_and_to_decode():
+    rng = np.random.default_rng(13)
+    H, D, B = 2, 8, 4
+    # No prefix: the same as causal prefill over the prompt's own K/V.
+    lens = [5, 9]
+    q, k, v = (rng.standard_normal((sum(lens), H, D)) for _ in range(3))
+    tables, kc, vc, nb = [], [], [], 0
+    a = 0
+    for L in lens:
+        kp, vp, t = _pool_from_contiguous(rng, k[a : a + L].transpose(1, 0, 2), v[a : a + L].transpose(1, 0, 2), B)
+        tables.append(t + nb); kc.append(kp); vc.append(vp); nb += kp.shape[0]; a += L
+    width = max(len(t) for t in tables)
+    tab = np.stack([np.pad(t, (0, width - len(t))) for t in tables])
+    got = A.prefix_prefill(q, np.concatenate(kc), np.concatenate(vc), tab, [0, 0], lens, 0.3, "f32", B)
+    ref = A.causal_prefill(q, k, v, lens, 0.3, "f32")
+    assert np.abs(got - ref).max() < 1e-13
+    # With a prefix: the last new token equals decode over the whole context, and
+    # the first new token sees exactly the prefix plus itself.
+    C, L = 11, 6
+    K = rng.standard_normal((H, C + L, D)); V = rng.standard_normal((H, C + L, D))
+    kp, vp, t = _pool_from_contiguous(rng, K, V, B)
+    qn = rng.standard_normal((L, H, D))
+    got = A.prefix_prefill(qn, kp, vp, t[None], [C], [L], 0.5, "f32", B)
+    dec = A.paged_decode(qn[-1:], kp, vp, t[None], np.array([C + L]), 0.5, "f32", B)
+    assert np.abs(got[-1] - dec[0]).max() < 1e-13
+    first = _sdpa(qn[0][:, None, :], K[:, : C + 1].copy(), V[:, : C + 1].copy(), 0.5)[:, 0, :]
+    assert np.abs(got[0] - first).max() < 1e-13
