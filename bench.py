@@ -21,6 +21,9 @@ The same line also carries:
                 the same step's sequences.
   mixed_step    the mixed prefill+decode step (8 prompts prefilled while 192
                 sequences decode), per kernel, with prefill's MFMA rate.
+  sharing_step  parallel sampling over shared prompt blocks: the batched
+                copy-on-write copy, then decode (logical and unique KV GB/s).
+  cached_prefix_prefill  requests prefilling over one cached shared prefix.
 """
 
 from __future__ import annotations
@@ -54,6 +57,7 @@ def _args():
     ap.add_argument("--partition", type=int, default=512)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-mixed", action="store_true")
+    ap.add_argument("--no-extras", action="store_true", help="skip the sharing and cached-prefix measurements")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="time box of the CPU oracle sample")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of a known size (for counter calibration) and exit")
@@ -208,6 +212,11 @@ def main() -> int:
     if not a.no_mixed:
         line["mixed_step"] = mixed_step(a, dev, up)
 
+    # ---------------- sharing, copy-on-write and cached-prefix prefill ----------------
+    if not a.no_extras:
+        line["sharing_step"] = sharing_step(a, dev, up)
+        line["cached_prefix_prefill"] = cached_prefix_prefill(a, dev, up)
+
     # ---------------- CPU oracle baseline ----------------
     if not a.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(d, a.cpu_seconds)
@@ -285,6 +294,105 @@ def mixed_step(a, dev, up):
         "prefill_mfma_frac": round(flops / (p_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
         "decode_GBps": round(dec_bytes / (d_ms * 1e-3) / 1e9, 1),
         "decode_tokens_attended_per_s": round(float(d.context_lens.sum()) / (d_ms * 1e-3), 1),
+    }
+
+
+def _time_events(fn, warmup, steps):
+    import torch
+
+    for _ in range(warmup):
+        fn()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(steps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def sharing_step(a, dev, up):
+    """Block sharing (OPT-13B head shape, fp16): 128 prompts x 4 parallel samples.
+
+    Each group's samples read the prompt's physical blocks; the partly filled
+    last prompt block is copied on write (batched pkv_copy_blocks), then every
+    sample decodes.  KV GB/s is reported against both the logical bytes (each
+    sample's whole context) and the unique bytes (distinct slots read).
+    """
+    import numpy as np
+    import torch
+
+    from paged_kv_cache_137_amd import ops
+    from paged_kv_cache_137_amd import workloads as W
+
+    d = W.decode_config(4, poison=False)
+    S, H, D = d.q.shape
+    pairs = up(d.info["cow_pairs"].astype(np.int64))
+    t = dict(q=up(d.q), kc=up(d.k_cache), vc=up(d.v_cache), bt=up(d.block_tables), cl=up(d.context_lens))
+    out = torch.empty((S, H, D), dtype=torch.float16, device=dev)
+    ws = torch.empty(ops.decode_workspace_bytes(S, H, D, d.max_context_len, 512), dtype=torch.uint8, device=dev)
+    copy_ms = _time_events(lambda: ops.copy_blocks(t["kc"], t["vc"], pairs), a.warmup, a.steps)
+    dec_ms = _time_events(lambda: ops.paged_attn_decode(t["q"], t["kc"], t["vc"], t["bt"], t["cl"], d.scale, out,
+                                                        max_context_len=d.max_context_len, partition_size=512,
+                                                        workspace=ws), a.warmup, a.steps)
+    used = np.zeros((d.num_blocks, 16), dtype=bool)
+    for s_ in range(S):
+        n = int(d.context_lens[s_])
+        nfull, rem = divmod(n, 16)
+        used[d.block_tables[s_, :nfull]] = True
+        if rem:
+            used[d.block_tables[s_, nfull], :rem] = True
+    per_tok = 2 * H * D * 2
+    logical = int(d.context_lens.sum()) * per_tok
+    unique = int(used.sum()) * per_tok
+    npairs = int(pairs.shape[0])
+    copy_bytes = npairs * H * 16 * D * 2 * 2 * 2
+    return {
+        "workload": "OPT-13B head shape (40 x 128), fp16, 128 prompts U[64,1024] x 4 samples, own tokens U[1,256]",
+        "copy_blocks_pairs": npairs,
+        "copy_blocks_ms": round(copy_ms, 5),
+        "copy_blocks_GBps": round(copy_bytes / (copy_ms * 1e-3) / 1e9, 1),
+        "decode_ms": round(dec_ms, 4),
+        "decode_logical_GBps": round(logical / (dec_ms * 1e-3) / 1e9, 1),
+        "decode_unique_GBps": round(unique / (dec_ms * 1e-3) / 1e9, 1),
+        "physical_blocks": d.info["physical_blocks_used"],
+        "logical_blocks": d.info["logical_blocks"],
+    }
+
+
+def cached_prefix_prefill(a, dev, up):
+    """16 requests share a cached 1024-token prefix; each prefills 256 new tokens (32 x 128, bf16)."""
+    import numpy as np
+    import torch
+
+    from paged_kv_cache_137_amd import ops
+    from paged_kv_cache_137_amd import workloads as W
+    from paged_kv_cache_137_amd.blocks import BlockManager
+
+    H, D, B, R, C, L = 32, 128, 16, 16, 1024, 256
+    nb = C // B + R * (L // B) + 8
+    m = BlockManager(nb, B, free_order=np.random.default_rng(5).permutation(nb))
+    m.add_sequence(-1, C)
+    for r in range(R):
+        m.fork(-1, r)
+        for _ in range(L):
+            m.append_token(r)
+    tables = up(m.block_tables(range(R), pad=0))
+    kc = up(W.normal((91, 1), (nb, H, B, D), "bf16"), "bf16")
+    vc = up(W.normal((91, 2), (nb, H, B, D), "bf16"), "bf16")
+    q = up(W.normal((91, 3), (R * L, H, D), "bf16"), "bf16")
+    out = torch.empty((R * L, H, D), dtype=torch.bfloat16, device=dev)
+    pre = up(np.full(R, C, np.int32))
+    lens = up(np.full(R, L, np.int32))
+    ms = _time_events(lambda: ops.paged_attn_prefill_cached(q, kc, vc, tables, pre, lens, out, max_prompt_len=L,
+                                                            max_prefix_len=C), a.warmup, a.steps)
+    flops = 4.0 * D * H * R * sum(C + i + 1 for i in range(L))
+    return {
+        "workload": "16 requests x 256 new tokens over one cached 1024-token prefix, 32 heads x 128, bf16",
+        "ms": round(ms, 4),
+        "TFLOPs": round(flops / (ms * 1e-3) / 1e12, 1),
+        "mfma_frac": round(flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
     }
 
 

@@ -43,7 +43,7 @@
  *  b * block_size + o.  One block table per sequence is shared by all heads of
  *  the layer: a physical id names the same block index in every head's slice.
  *
- * Supported: block_size 16; head_dim 64 or 128; dtype f32, f16 or bf16 for the
+ * Supported: block_size 8, 16 (the default) or 32; head_dim 64 or 128; dtype f32, f16 or bf16 for the
  * write and decode; f16 or bf16 for prefill.  Output dtype: f32, or the input
  * dtype.  Accumulation is always in f32, and the result is rounded once
  * (nearest-even) when stored.
@@ -145,8 +145,8 @@ size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t h
  *                 max_context_len <= max_blocks_per_seq * block_size
  *   scale         multiplies q.k before the softmax (usually 1/sqrt(head_dim))
  *   out           [num_seqs][num_heads][head_dim] of out_dtype (PKV_F32 or desc->dtype)
- *   partition_size  tokens per context partition, a multiple of 16 between 16 and
- *                 4096, or 0 for no split.  Each (sequence, head, partition)
+ *   partition_size  tokens per context partition: a multiple of the block size,
+ *                 between 16 and 4096, or 0 for no split.  Each (sequence, head, partition)
  *                 is one workgroup.  A sequence spanning more than one partition
  *                 is merged by a second, reduce kernel (max-rescaled sum of the
  *                 partial results), in a fixed order.
@@ -264,6 +264,33 @@ int pkv_paged_attn_prefill_cached(const void* q, const void* k_cache, const void
  * no-op.
  */
 int pkv_copy_blocks(void* k_cache, void* v_cache, const pkv_cache_desc* desc, const int64_t* block_pairs,
+                    int64_t num_pairs, void* stream);
+
+/*
+ * pkv_swap_blocks - move whole blocks between two pools (swap out / swap in).
+ *
+ * When memory runs out, a preempted sequence's blocks are evicted all
+ * together.  With swapping, they are copied to a pool in CPU memory and
+ * brought back later, possibly into different physical blocks ("vLLM &
+ * PagedAttention ...", section VIII; P1 section 4.5).  This call copies the
+ * (source block, destination block) pairs from one pool to another, all
+ * heads, keys and values, in one launch.  Either pool may be device memory or
+ * pinned host memory (hipHostMalloc, or torch's pin_memory); the GPU reads or
+ * writes host memory directly over the bus.
+ *
+ *   src_k, src_v      source pool, [src_num_blocks][H][B][D] as desc describes
+ *   dst_k, dst_v      destination pool, [dst_num_blocks][H][B][D]
+ *   desc              num_heads, head_dim, block_size and dtype of both pools
+ *                     (its num_blocks is not used)
+ *   block_pairs       int64 [num_pairs][2] = (source block, destination block), in
+ *                     device memory or pinned host memory
+ * Pairs with an id outside its pool are skipped.  Destinations must be
+ * distinct.  A pool pointer that is neither device memory nor pinned host
+ * memory returns PKV_EINVAL before anything is launched.  num_pairs == 0 is a
+ * no-op.
+ */
+int pkv_swap_blocks(const void* src_k, const void* src_v, int64_t src_num_blocks, void* dst_k, void* dst_v,
+                    int64_t dst_num_blocks, const pkv_cache_desc* desc, const int64_t* block_pairs,
                     int64_t num_pairs, void* stream);
 
 #ifdef __cplusplus

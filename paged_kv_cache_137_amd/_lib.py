@@ -29,6 +29,7 @@ SIGNATURES = {
     "pkv_paged_attn_decode_partial": (_DECODE_ARGS, ctypes.c_int),
     "pkv_paged_attn_decode_reduce": (_DECODE_ARGS, ctypes.c_int),
     "pkv_copy_blocks": ([_vp, _vp, _vp, _vp, _i64, _vp], ctypes.c_int),
+    "pkv_swap_blocks": ([_vp, _vp, _i64, _vp, _vp, _i64, _vp, _vp, _i64, _vp], ctypes.c_int),
     "pkv_paged_attn_prefill_cached": (
         [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32, _i64, _i32, _i32, _f32, _vp, _i32, _vp],
         ctypes.c_int,

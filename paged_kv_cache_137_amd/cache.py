@@ -16,8 +16,8 @@ from . import ops
 class PagedKVCache:
     def __init__(self, num_blocks: int, num_heads: int, head_dim: int, block_size: int = 16,
                  dtype: torch.dtype = torch.bfloat16, device="cuda"):
-        if block_size != ops.BLOCK_SIZE:
-            raise ValueError(f"block_size must be {ops.BLOCK_SIZE}")
+        if block_size not in ops.BLOCK_SIZES:
+            raise ValueError(f"block_size must be one of {ops.BLOCK_SIZES}")
         shape = (num_blocks, num_heads, block_size, head_dim)
         self.k_cache = torch.empty(shape, dtype=dtype, device=device)
         self.v_cache = torch.empty(shape, dtype=dtype, device=device)

@@ -6,6 +6,10 @@
 // Serving", section VII, Figure 8).  The copies of one step are batched into a
 // single kernel rather than one small memory copy each (section X).
 //
+// The same kernel moves blocks between two pools, one of which may be pinned
+// host memory: the swap-out and swap-in of a preempted sequence's blocks
+// (section VIII of the same page).
+//
 // Decomposition: one workgroup per (pair, head).  Its 256 lanes move the 4 KiB
 // (block, head) tile of keys and the one of values in 16-byte chunks, with a
 // loop when a tile is larger (fp32 with head_dim 128).  Both tiles are
@@ -21,14 +25,14 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(const CopyArgs a, int6
   const int h = blockIdx.y;
   const int64_t src = a.pairs[2 * pr];
   const int64_t dst = a.pairs[2 * pr + 1];
-  if (src < 0 || src >= a.num_blocks || dst < 0 || dst >= a.num_blocks) return;
+  if (src < 0 || src >= a.src_blocks || dst < 0 || dst >= a.dst_blocks) return;
   const int64_t tile = a.tile_bytes;
   const int64_t so = (src * a.num_heads + h) * tile;
   const int64_t dof = (dst * a.num_heads + h) * tile;
-  const char* ks = reinterpret_cast<const char*>(a.k_cache) + so;
-  const char* vs = reinterpret_cast<const char*>(a.v_cache) + so;
-  char* kd = reinterpret_cast<char*>(a.k_cache) + dof;
-  char* vd = reinterpret_cast<char*>(a.v_cache) + dof;
+  const char* ks = reinterpret_cast<const char*>(a.src_k) + so;
+  const char* vs = reinterpret_cast<const char*>(a.src_v) + so;
+  char* kd = reinterpret_cast<char*>(a.dst_k) + dof;
+  char* vd = reinterpret_cast<char*>(a.dst_v) + dof;
   for (int off = threadIdx.x * 16; off < a.tile_bytes; off += 256 * 16) {
     const uint4 kx = *reinterpret_cast<const uint4*>(ks + off);
     const uint4 vx = *reinterpret_cast<const uint4*>(vs + off);

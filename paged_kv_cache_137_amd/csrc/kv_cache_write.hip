@@ -4,8 +4,8 @@
 // This is the fused reshape-and-block-write step of "vLLM & PagedAttention:
 // Efficient Memory Management for LLM Serving", section X.  The new K/V arrive
 // as [token][head][dim].  Each (token, head) row moves as one D*elem-byte run
-// to cache[slot / 16][head][slot % 16][:], for keys and values in the same
-// kernel, in one launch.
+// to cache[slot / B][head][slot % B][:] (B tokens per block), for keys and
+// values in the same kernel, in one launch.
 //
 // Decomposition: one lane per 16-byte chunk of a (token, head) row, keys and
 // values both.  A wavefront therefore reads 1 KiB of consecutive source bytes
@@ -27,8 +27,9 @@ __global__ __launch_bounds__(256) void kv_cache_write_kernel(const WriteArgs a, 
   const int32_t h = row - tl * a.num_heads;
   const int64_t t = tok0 + tl;
   const int64_t slot = a.slot_mapping[t];
-  if (slot < 0 || slot >= a.num_blocks * 16) return;  // padding token, or a slot outside the pool
-  const int64_t dst = (((slot >> 4) * a.num_heads + h) * 16 + (slot & 15)) * CPR + c;
+  const int sh = a.block_shift;
+  if (slot < 0 || slot >= (a.num_blocks << sh)) return;  // padding token, or a slot outside the pool
+  const int64_t dst = ((((slot >> sh) * a.num_heads + h) << sh) + (slot & ((1 << sh) - 1))) * CPR + c;
   const int64_t src = (t * a.num_heads + h) * CPR + c;
   const uint4 kx = reinterpret_cast<const uint4*>(a.k)[src];
   const uint4 vx = reinterpret_cast<const uint4*>(a.v)[src];

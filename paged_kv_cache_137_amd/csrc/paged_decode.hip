@@ -19,7 +19,8 @@
 //    results are deterministic.
 //  - Inside a unit, wave w takes the partition's blocks w, w+4, w+8, ..., so a
 //    short partition still spreads over all waves.
-//  - A (block, head) tile is 16 tokens x D values stored contiguously.  A wave
+//  - A (block, head) tile is BS tokens x D values stored contiguously (BS = 16
+//    by default; 8 and 32 are built too).  A wave
 //    reads it with NI 16-byte loads per lane, each load instruction covering
 //    1 KiB of consecutive bytes.  Lane l holds dims (l % LPT)*VEC .. +VEC of
 //    token row l / LPT.  K/V are read with the nontemporal hint: every tile is
@@ -51,7 +52,6 @@ namespace pkv {
 #define PKV_DEC_PP 1
 #endif
 
-constexpr int BS = 16;             // tokens per block
 constexpr int NW = PKV_DEC_NW;     // wavefronts per workgroup
 constexpr int PLAN_BUCKETS = 257;  // partition sizes 0..256 blocks (larger ones share the top bucket)
 
@@ -65,7 +65,7 @@ __device__ __forceinline__ uint4 load_kv16(const char* p) {
 #endif
 }
 
-template <typename E, int D>
+template <typename E, int D, int BS>
 struct DecodeGeom {
   static constexpr int ES = E::bytes;
   static constexpr int VEC = 16 / ES;      // elements per 16-byte chunk
@@ -74,6 +74,10 @@ struct DecodeGeom {
   static constexpr int NI = BS / TPI;      // loads per tile
   static constexpr int TILE = BS * D * ES; // bytes of one (block, head) tile
   static_assert(TPI * LPT == 64 && NI * TPI == BS, "tile must map onto a wavefront");
+  // Two register sets (load the next tile while consuming this one) while a
+  // tile is small; one set for large tiles, where the registers would cost
+  // more occupancy than the overlap gains.
+  static constexpr bool PINGPONG = PKV_DEC_PP && NI <= 4;
 };
 
 __device__ __forceinline__ int clamp_ctx(const DecodeArgs& a, int s) { return min(a.context_lens[s], a.max_context_len); }
@@ -83,6 +87,7 @@ __device__ __forceinline__ int clamp_ctx(const DecodeArgs& a, int s) { return mi
 // (partition 0, in the smallest bucket) so that its output is written as NaN.
 __global__ __launch_bounds__(1024) void decode_plan_kernel(const DecodeArgs a) {
   __shared__ int cnt[PLAN_BUCKETS];
+  const int BS = a.block_size;
   const int part_tokens = a.part_blocks * BS;
   for (int i = threadIdx.x; i < PLAN_BUCKETS; i += blockDim.x) cnt[i] = 0;
   __syncthreads();
@@ -139,9 +144,9 @@ __global__ __launch_bounds__(1024) void decode_plan_kernel(const DecodeArgs a) {
   }
 }
 
-template <typename E, typename O, int D>
+template <typename E, typename O, int D, int BS>
 __global__ __launch_bounds__(NW * 64) void decode_partial_kernel(const DecodeArgs a) {
-  using G = DecodeGeom<E, D>;
+  using G = DecodeGeom<E, D, BS>;
   using C = Chunk<E>;
   constexpr int VEC = G::VEC, LPT = G::LPT, TPI = G::TPI, NI = G::NI;
   constexpr int ROWS = NW * TPI;  // online-softmax states per workgroup
@@ -250,7 +255,7 @@ __global__ __launch_bounds__(NW * 64) void decode_partial_kernel(const DecodeArg
       };
       int j = w;
       if (j >= cn) continue;
-#if PKV_DEC_PP
+      if constexpr (G::PINGPONG) {
       uint4 kA[NI], vA[NI], kB[NI], vB[NI];
       bool badA, badB;
       load(phys_of(j, badA), kA, vA);
@@ -268,14 +273,14 @@ __global__ __launch_bounds__(NW * 64) void decode_partial_kernel(const DecodeArg
       } else {
         consume(kA, vA, cb + j, badA);
       }
-#else
+      } else {
       for (; j < cn; j += NW) {
         uint4 kA[NI], vA[NI];
         bool badA;
         load(phys_of(j, badA), kA, vA);
         consume(kA, vA, cb + j, badA);
       }
-#endif
+      }
     }
 
     // Merge the ROWS running states of this unit: max, rescaled sums.
@@ -323,7 +328,7 @@ __global__ __launch_bounds__(D) void decode_reduce_kernel(const DecodeArgs a) {
   const int h = blockIdx.y;
   const int ctx = clamp_ctx(a, s);
   if (ctx <= 0) return;
-  const int part_tokens = a.part_blocks * BS;
+  const int part_tokens = a.part_blocks * a.block_size;
   const int nparts = (ctx + part_tokens - 1) / part_tokens;
   if (nparts <= 1) return;
   const int t = threadIdx.x;
@@ -359,12 +364,19 @@ static int persistent_grid(K kernel, int block, int64_t units) {
   return (int)(units < n ? units : n);
 }
 
+template <typename E, typename O, int D, int BS>
+static hipError_t partial_bs(const DecodeArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(1024), 0, st, a);
+  const int grid = persistent_grid(decode_partial_kernel<E, O, D, BS>, NW * 64, a.total_units);
+  hipLaunchKernelGGL((decode_partial_kernel<E, O, D, BS>), dim3(grid), dim3(NW * 64), 0, st, a);
+  return hipGetLastError();
+}
+
 template <typename E, typename O, int D>
 static hipError_t partial_t(const DecodeArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(1024), 0, st, a);
-  const int grid = persistent_grid(decode_partial_kernel<E, O, D>, NW * 64, a.total_units);
-  hipLaunchKernelGGL((decode_partial_kernel<E, O, D>), dim3(grid), dim3(NW * 64), 0, st, a);
-  return hipGetLastError();
+  if (a.block_size == 8) return partial_bs<E, O, D, 8>(a, st);
+  if (a.block_size == 32) return partial_bs<E, O, D, 32>(a, st);
+  return partial_bs<E, O, D, 16>(a, st);
 }
 
 template <typename O, int D>

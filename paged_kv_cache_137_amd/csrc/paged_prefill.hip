@@ -39,8 +39,8 @@
 //  - Query tiles are dispatched longest-first (descending tile index), to even
 //    out the causal triangle's load.
 //  - Cached-prefix variant: keys and values are gathered from the paged pool
-//    through the prompt's block table.  Each 16-key run is one contiguous
-//    (block, head) tile.  Positions before the prompt's new tokens are a
+//    through the prompt's block table.  Each block's run of keys is one
+//    contiguous (block, head) tile.  Positions before the prompt's new tokens are a
 //    shared prefix that is already cached ("vLLM & PagedAttention ...",
 //    section VII: the prompt phase runs only over the request's own input).
 //    The causal limit is then shifted by the prefix length.
@@ -176,7 +176,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
   int C = 0;
   const int32_t* trow = nullptr;
   if constexpr (PAGED) {
-    const int cap = a.max_blocks_per_seq * 16;
+    const int cap = a.max_blocks_per_seq << a.block_shift;
     C = a.prefix_lens != nullptr ? min(max(a.prefix_lens[pr], 0), cap) : 0;
     L = min(L, cap - C);
     trow = a.block_tables + (int64_t)pr * a.max_blocks_per_seq;
@@ -238,9 +238,9 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
       const uint4 nanv = make_uint4(E16_NAN2, E16_NAN2, E16_NAN2, E16_NAN2);
       auto fetch = [&](const void* pool, int key, int ch) -> uint4 {
         if (key >= C + L) return make_uint4(0u, 0u, 0u, 0u);
-        const int ph = trow[key >> 4];
+        const int ph = trow[key >> a.block_shift];
         if ((uint64_t)(uint32_t)ph >= (uint64_t)a.num_blocks) return nanv;
-        const int64_t row = ((int64_t)ph * a.num_heads + h) * 16 + (key & 15);
+        const int64_t row = (((int64_t)ph * a.num_heads + h) << a.block_shift) + (key & ((1 << a.block_shift) - 1));
         return *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(pool) + row * (D * 2) + ch * 16);
       };
 #pragma unroll

@@ -45,12 +45,14 @@ int check_desc(const pkv_cache_desc* d) {
   if (d == nullptr) return PKV_EINVAL;
   if (d->num_blocks <= 0 || d->num_heads <= 0 || d->head_dim <= 0 || d->block_size <= 0) return PKV_EINVAL;
   if (!valid_dtype(d->dtype)) return PKV_EINVAL;
-  if (d->block_size != kBlock) return PKV_ENOTSUP;
+  if (d->block_size != 8 && d->block_size != 16 && d->block_size != 32) return PKV_ENOTSUP;
   if (d->head_dim != 64 && d->head_dim != 128) return PKV_ENOTSUP;
   return PKV_OK;
 }
 
 int launch_status(hipError_t e) { return e == hipSuccess ? PKV_OK : PKV_ELAUNCH; }
+
+int log2_block(int32_t b) { return b == 8 ? 3 : b == 32 ? 5 : 4; }
 
 template <typename T>
 bool copy_to_host(std::vector<T>& dst, const T* src, size_t n, hipStream_t st) {
@@ -75,13 +77,13 @@ struct DecodePlan {
 size_t align16(size_t x) { return (x + 15) & ~(size_t)15; }
 
 DecodePlan plan_decode(int32_t num_seqs, int32_t num_heads, int32_t head_dim, int32_t max_context_len,
-                       int32_t partition_size) {
+                       int32_t partition_size, int32_t block_size = kBlock) {
   DecodePlan p;
   if (partition_size == 0) {
-    p.part_blocks = (max_context_len + kBlock - 1) / kBlock;
+    p.part_blocks = (max_context_len + block_size - 1) / block_size;
     p.num_parts = 1;
   } else {
-    p.part_blocks = partition_size / kBlock;
+    p.part_blocks = partition_size / block_size;
     p.num_parts = (max_context_len + partition_size - 1) / partition_size;
   }
   const size_t units = (size_t)num_seqs * num_heads * p.num_parts;
@@ -101,15 +103,17 @@ int decode_impl(int stages, const void* q, const void* k_cache, const void* v_ca
   int st = check_desc(desc);
   if (st != PKV_OK) return st;
   if (num_seqs < 0 || max_blocks_per_seq <= 0 || max_context_len <= 0) return PKV_EINVAL;
-  if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * kBlock) return PKV_EINVAL;
+  const int32_t bsz = desc->block_size;
+  if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * bsz) return PKV_EINVAL;
   if (out_dtype != PKV_F32 && out_dtype != desc->dtype) return PKV_ENOTSUP;
-  if (partition_size != 0 && (partition_size % kBlock != 0 || partition_size < kBlock || partition_size > 4096))
+  if (partition_size != 0 && (partition_size % bsz != 0 || partition_size < 16 || partition_size > 4096))
     return PKV_EINVAL;
   if (num_seqs == 0) return PKV_OK;
   if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out) return PKV_EINVAL;
   if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16)) return PKV_EINVAL;
   if (!aligned(block_tables, 4) || !aligned(context_lens, 4)) return PKV_EINVAL;
-  const DecodePlan plan = plan_decode(num_seqs, desc->num_heads, desc->head_dim, max_context_len, partition_size);
+  const DecodePlan plan =
+      plan_decode(num_seqs, desc->num_heads, desc->head_dim, max_context_len, partition_size, bsz);
   const int64_t units = (int64_t)num_seqs * desc->num_heads * plan.num_parts;
   if (units > ((int64_t)1 << 31) - 64 || num_seqs > 65535 * 32768) return PKV_EINVAL;
   if (desc->num_heads > 65535) return PKV_EINVAL;
@@ -125,7 +129,7 @@ int decode_impl(int stages, const void* q, const void* k_cache, const void* v_ca
     if (!copy_to_host(tab, block_tables, (size_t)num_seqs * max_blocks_per_seq, sm)) return PKV_EDEVICE;
     for (int32_t s = 0; s < num_seqs; ++s) {
       if (lens[s] < 1 || lens[s] > max_context_len) return PKV_EINVAL;
-      const int32_t nb = (lens[s] + kBlock - 1) / kBlock;
+      const int32_t nb = (lens[s] + bsz - 1) / bsz;
       for (int32_t j = 0; j < nb; ++j) {
         const int32_t b = tab[(size_t)s * max_blocks_per_seq + j];
         if (b < 0 || b >= desc->num_blocks) return PKV_EINVAL;
@@ -150,6 +154,7 @@ int decode_impl(int stages, const void* q, const void* k_cache, const void* v_ca
   a.max_blocks_per_seq = max_blocks_per_seq;
   a.num_seqs = num_seqs;
   a.max_context_len = max_context_len;
+  a.block_size = bsz;
   a.part_blocks = plan.part_blocks;
   a.num_parts = plan.num_parts;
   a.total_units = (int32_t)units;
@@ -205,7 +210,7 @@ int pkv_kv_cache_write(const void* k, const void* v, const int64_t* slot_mapping
     used.reserve(slots.size());
     for (int64_t x : slots) {
       if (x < 0) continue;
-      if (x >= desc->num_blocks * kBlock) return PKV_EINVAL;
+      if (x >= desc->num_blocks * desc->block_size) return PKV_EINVAL;
       used.push_back(x);
     }
     std::sort(used.begin(), used.end());
@@ -222,13 +227,13 @@ int pkv_kv_cache_write(const void* k, const void* v, const int64_t* slot_mapping
   a.num_heads = desc->num_heads;
   a.head_dim = desc->head_dim;
   a.dtype = desc->dtype;
+  a.block_shift = log2_block(desc->block_size);
   return launch_status(pkv::launch_kv_cache_write(a, sm));
 }
 
 size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim, int32_t max_context_len,
                                   int32_t partition_size) {
   if (num_seqs <= 0 || num_heads <= 0 || head_dim <= 0 || max_context_len <= 0 || partition_size < 0) return 0;
-  if (partition_size != 0 && partition_size % kBlock != 0) return 0;
   return plan_decode(num_seqs, num_heads, head_dim, max_context_len, partition_size).ws_bytes;
 }
 
@@ -272,7 +277,7 @@ int pkv_paged_attn_prefill(const void* q, const void* k, const void* v, int32_t 
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) || !aligned(prompt_lens, 4))
     return PKV_EINVAL;
   if (block_tables != nullptr &&
-      (max_blocks_per_seq <= 0 || (int64_t)max_blocks_per_seq * kBlock < (int64_t)max_prompt_len))
+      max_blocks_per_seq <= 0)
     return PKV_EINVAL;
   const int32_t num_qtiles = (max_prompt_len + pkv::PREFILL_BLOCK_M - 1) / pkv::PREFILL_BLOCK_M;
   const int64_t items = (int64_t)num_qtiles * num_heads * num_prompts;
@@ -325,7 +330,7 @@ int pkv_paged_attn_prefill_cached(const void* q, const void* k_cache, const void
       !aligned(prompt_lens, 4) || !aligned(block_tables, 4) || !aligned(prefix_lens, 4))
     return PKV_EINVAL;
   if (max_blocks_per_seq <= 0 ||
-      (int64_t)max_blocks_per_seq * kBlock < (int64_t)max_prompt_len + (int64_t)max_prefix_len)
+      (int64_t)max_blocks_per_seq * desc->block_size < (int64_t)max_prompt_len + (int64_t)max_prefix_len)
     return PKV_EINVAL;
   const int32_t num_qtiles = (max_prompt_len + pkv::PREFILL_BLOCK_M - 1) / pkv::PREFILL_BLOCK_M;
   const int64_t items = (int64_t)num_qtiles * desc->num_heads * num_prompts;
@@ -343,7 +348,7 @@ int pkv_paged_attn_prefill_cached(const void* q, const void* k_cache, const void
       const int32_t L = lens[p], C = prefix_lens ? pre[p] : 0;
       if (L < 0 || L > max_prompt_len || C < 0 || C > max_prefix_len) return PKV_EINVAL;
       sum += L;
-      for (int32_t j = 0; j < (C + L + kBlock - 1) / kBlock; ++j) {
+      for (int32_t j = 0; j < (C + L + desc->block_size - 1) / desc->block_size; ++j) {
         const int32_t b = tab[(size_t)p * max_blocks_per_seq + j];
         if (b < 0 || b >= desc->num_blocks) return PKV_EINVAL;
       }
@@ -358,6 +363,7 @@ int pkv_paged_attn_prefill_cached(const void* q, const void* k_cache, const void
   a.prefix_lens = prefix_lens;
   a.num_blocks = desc->num_blocks;
   a.max_blocks_per_seq = max_blocks_per_seq;
+  a.block_shift = log2_block(desc->block_size);
   a.prompt_lens = prompt_lens;
   a.out = out;
   a.total_tokens = total_tokens;
@@ -400,13 +406,67 @@ int pkv_copy_blocks(void* k_cache, void* v_cache, const pkv_cache_desc* desc, co
       if (std::binary_search(srcs.begin(), srcs.end(), d0)) return PKV_EINVAL;
   }
   pkv::CopyArgs a{};
-  a.k_cache = k_cache;
-  a.v_cache = v_cache;
+  a.src_k = k_cache;
+  a.src_v = v_cache;
+  a.dst_k = k_cache;
+  a.dst_v = v_cache;
   a.pairs = block_pairs;
   a.num_pairs = num_pairs;
-  a.num_blocks = desc->num_blocks;
+  a.src_blocks = desc->num_blocks;
+  a.dst_blocks = desc->num_blocks;
   a.num_heads = desc->num_heads;
   a.tile_bytes = desc->block_size * desc->head_dim * (desc->dtype == PKV_F32 ? 4 : 2);
+  return launch_status(pkv::launch_copy_blocks(a, sm));
+}
+
+int pkv_swap_blocks(const void* src_k, const void* src_v, int64_t src_num_blocks, void* dst_k, void* dst_v,
+                    int64_t dst_num_blocks, const pkv_cache_desc* desc, const int64_t* block_pairs,
+                    int64_t num_pairs, void* stream) {
+  if (desc == nullptr) return PKV_EINVAL;
+  pkv_cache_desc d = *desc;
+  d.num_blocks = 1;
+  int st = check_desc(&d);
+  if (st != PKV_OK) return st;
+  if (num_pairs < 0 || src_num_blocks <= 0 || dst_num_blocks <= 0) return PKV_EINVAL;
+  if (num_pairs == 0) return PKV_OK;
+  if (!src_k || !src_v || !dst_k || !dst_v || !block_pairs) return PKV_EINVAL;
+  if (!aligned(src_k, 16) || !aligned(src_v, 16) || !aligned(dst_k, 16) || !aligned(dst_v, 16) ||
+      !aligned(block_pairs, 8))
+    return PKV_EINVAL;
+  if (d.num_heads > 65535) return PKV_EINVAL;
+  st = device_status();
+  if (st != PKV_OK) return st;
+  // Every pointer the kernel dereferences must be device memory or pinned host
+  // memory; use the device-side address of pinned host memory.
+  const void* ptrs[5] = {src_k, src_v, dst_k, dst_v, block_pairs};
+  void* dev_ptrs[5];
+  for (int i = 0; i < 5; ++i) {
+    hipPointerAttribute_t attr;
+    if (hipPointerGetAttributes(&attr, ptrs[i]) != hipSuccess) {
+      (void)hipGetLastError();  // clear the query's error state
+      return PKV_EINVAL;
+    }
+    if (attr.type == hipMemoryTypeDevice) {
+      dev_ptrs[i] = const_cast<void*>(ptrs[i]);
+    } else if (attr.type == hipMemoryTypeHost && attr.devicePointer != nullptr) {
+      const char* base_h = reinterpret_cast<const char*>(attr.hostPointer);
+      dev_ptrs[i] = reinterpret_cast<char*>(attr.devicePointer) + (reinterpret_cast<const char*>(ptrs[i]) - base_h);
+    } else {
+      return PKV_EINVAL;
+    }
+  }
+  hipStream_t sm = reinterpret_cast<hipStream_t>(stream);
+  pkv::CopyArgs a{};
+  a.src_k = dev_ptrs[0];
+  a.src_v = dev_ptrs[1];
+  a.dst_k = dev_ptrs[2];
+  a.dst_v = dev_ptrs[3];
+  a.pairs = reinterpret_cast<const int64_t*>(dev_ptrs[4]);
+  a.num_pairs = num_pairs;
+  a.src_blocks = src_num_blocks;
+  a.dst_blocks = dst_num_blocks;
+  a.num_heads = d.num_heads;
+  a.tile_bytes = d.block_size * d.head_dim * (d.dtype == PKV_F32 ? 4 : 2);
   return launch_status(pkv::launch_copy_blocks(a, sm));
 }
 

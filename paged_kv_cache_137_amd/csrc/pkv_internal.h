@@ -18,6 +18,7 @@ struct WriteArgs {
   int32_t num_heads;
   int32_t head_dim;
   int32_t dtype;
+  int32_t block_shift;  // log2(tokens per block)
 };
 
 // Arguments shared by the two decode stages.
@@ -37,6 +38,7 @@ struct DecodeArgs {
   int32_t max_blocks_per_seq;
   int32_t num_seqs;
   int32_t max_context_len;
+  int32_t block_size;   // tokens per block: 8, 16 or 32
   int32_t part_blocks;  // blocks per partition
   int32_t num_parts;    // P: partitions of the longest allowed context
   int32_t total_units;  // upper bound on units: H * S * P
@@ -55,6 +57,7 @@ struct PrefillArgs {
   const int32_t* prefix_lens;  // may be null: no prefix
   int64_t num_blocks;
   int32_t max_blocks_per_seq;
+  int32_t block_shift;  // log2(tokens per block) of the pool
   const int32_t* prompt_lens;
   void* out;
   int64_t total_tokens;
@@ -67,12 +70,17 @@ struct PrefillArgs {
   float scale_log2;
 };
 
+// Block copies from a source pool to a destination pool (the same pool for
+// copy-on-write).
 struct CopyArgs {
-  void* k_cache;
-  void* v_cache;
+  const void* src_k;
+  const void* src_v;
+  void* dst_k;
+  void* dst_v;
   const int64_t* pairs;  // [num_pairs][2] (src, dst)
   int64_t num_pairs;
-  int64_t num_blocks;
+  int64_t src_blocks;
+  int64_t dst_blocks;
   int32_t num_heads;
   int32_t tile_bytes;  // block_size * head_dim * element bytes
 };

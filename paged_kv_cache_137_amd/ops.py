@@ -15,7 +15,8 @@ import torch
 from . import _lib
 from ._lib import CacheDesc, check, lib
 
-BLOCK_SIZE = 16
+BLOCK_SIZE = 16           # the default block size (tokens per block)
+BLOCK_SIZES = (8, 16, 32)  # block sizes the library is built for
 DEFAULT_PARTITION = 512
 
 _DT = {torch.float32: _lib.PKV_F32, torch.float16: _lib.PKV_F16, torch.bfloat16: _lib.PKV_BF16}
@@ -235,3 +236,34 @@ def paged_attn_prefill_cached(q, k_cache, v_cache, block_tables, prefix_lens, pr
             _ptr(prefix_lens), _ptr(prompt_lens), P, T, int(max_prompt_len), int(max_prefix_len), float(scale),
             _ptr(out), pkv_dtype(out.dtype), _stream(dev)))
     return out
+
+
+def swap_blocks(src_k: torch.Tensor, src_v: torch.Tensor, dst_k: torch.Tensor, dst_v: torch.Tensor,
+                block_pairs: torch.Tensor, device=None) -> None:
+    """Copy (src block, dst block) pairs from one pool to another, in one launch.
+
+    Either pool may live on the GPU or in pinned host memory
+    (torch.empty(..., pin_memory=True)); block_pairs (int64 [n][2]) likewise.
+    The copy runs on `device`'s current stream (by default, the GPU pool's
+    device).  This is the swap-out / swap-in of a preempted sequence's blocks.
+    """
+    for name, t in (("src_k", src_k), ("src_v", src_v), ("dst_k", dst_k), ("dst_v", dst_v)):
+        if not isinstance(t, torch.Tensor) or t.dim() != 4 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous [blocks][H][B][D] tensor")
+        if not t.is_cuda and not t.is_pinned():
+            raise ValueError(f"{name} must be on the GPU or in pinned host memory")
+    if src_k.shape != src_v.shape or dst_k.shape != dst_v.shape or src_k.shape[1:] != dst_k.shape[1:]:
+        raise ValueError("pools must agree in [H][B][D]")
+    if len({src_k.dtype, src_v.dtype, dst_k.dtype, dst_v.dtype}) != 1:
+        raise ValueError("pools must share one dtype")
+    if block_pairs.dtype != torch.int64 or block_pairs.dim() != 2 or block_pairs.shape[1] != 2:
+        raise ValueError("block_pairs must be int64 [n][2]")
+    if not block_pairs.is_cuda and not block_pairs.is_pinned():
+        raise ValueError("block_pairs must be on the GPU or in pinned host memory")
+    if device is None:
+        device = next((t.device for t in (src_k, dst_k, block_pairs) if t.is_cuda), torch.device("cuda", 0))
+    desc = cache_desc(src_k)
+    with torch.cuda.device(device):
+        check("pkv_swap_blocks", lib().pkv_swap_blocks(
+            _ptr(src_k), _ptr(src_v), src_k.shape[0], _ptr(dst_k), _ptr(dst_v), dst_k.shape[0], ctypes.byref(desc),
+            _ptr(block_pairs), block_pairs.shape[0], _stream(device)))

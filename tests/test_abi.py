@@ -71,7 +71,7 @@ def test_bad_arguments_rejected_before_any_launch(lib):
     # NULL descriptor
     assert lib.pkv_kv_cache_write(null, null, null, 1, null, null, None, null) == _lib.PKV_EINVAL
     # unsupported block size / head dim
-    bad_b = _lib.CacheDesc(64, 4, 128, 8, _lib.PKV_BF16)
+    bad_b = _lib.CacheDesc(64, 4, 128, 12, _lib.PKV_BF16)
     assert lib.pkv_kv_cache_write(null, null, null, 1, null, null, ctypes.byref(bad_b), null) == _lib.PKV_ENOTSUP
     bad_d = _lib.CacheDesc(64, 4, 96, 16, _lib.PKV_BF16)
     assert lib.pkv_kv_cache_write(null, null, null, 1, null, null, ctypes.byref(bad_d), null) == _lib.PKV_ENOTSUP

@@ -240,3 +240,29 @@ def test_closed_forms_on_gpu():
         n = int(d.context_lens[s])
         mean = oracle.attention.gather(d.v_cache, d.block_tables[s], n, 16).astype(np.float64).mean(axis=1)
         assert np.abs(out[s] - mean).max() <= 1e-5
+
+
+@pytest.mark.parametrize("bs", [8, 32])
+@pytest.mark.parametrize("dt,D", [("bf16", 128), ("f16", 64), ("f32", 128)])
+def test_block_size_variants(bs, dt, D):
+    """Blocks of 8 and 32 tokens: write the current tokens, copy blocks, decode."""
+    print(f"block size {bs} {dt} D={D}", flush=True)
+    lens = [1, bs - 1, bs, bs + 1, 100, 511, 512, 513, 2000]
+    d = W.make_decode(91 + bs, dt, 4, D, lens, block_size=bs, with_new_tokens=True)
+    t = upload_decode(d)
+    sm = slot_mapping(d.block_tables, range(d.num_seqs), d.context_lens - 1, bs)
+    ops.kv_cache_write(up(d.k_new, dt), up(d.v_new, dt), up(sm), t["k_cache"], t["v_cache"])
+    kc, vc = oracle.attention.cache_write(d.k_cache, d.v_cache, d.k_new, d.v_new, sm, bs)
+    assert np.array_equal(bits(down(t["k_cache"])), bits(kc))
+    for part in (512, 0):
+        out32 = run_decode(ops, t, d, "f32", partition_size=part)
+        ref = oracle.attention.paged_decode(d.q, kc, vc, d.block_tables, d.context_lens, d.scale, dt, block_size=bs)
+        got = down(out32)
+        assert np.isfinite(got).all()
+        assert np.abs(got - ref).max() <= TOL[dt]
+    # block copies of the new block size
+    unused = sorted(set(range(d.num_blocks)) - set(d.block_tables.ravel().tolist()))
+    pairs = np.stack([d.block_tables[:3, 0], np.asarray(unused[:3])], axis=1).astype(np.int64)
+    ops.copy_blocks(t["k_cache"], t["v_cache"], up(pairs))
+    ek, ev = oracle.attention.copy_blocks(kc, vc, pairs)
+    assert np.array_equal(bits(down(t["k_cache"])), bits(ek)) and np.array_equal(bits(down(t["v_cache"])), bits(ev))

@@ -101,3 +101,58 @@ def test_multi_step_decode_with_fork_cow_and_free(dt):
         assert err <= TOL[dt], (step, err)
         assert np.array_equal(bits(down(dk)), bits(host_k)) and np.array_equal(bits(down(dv)), bits(host_v))
     assert sum(1 for _ in m.tables) == len(live)
+
+
+def test_swap_out_to_pinned_host_and_back_in():
+    """Preemption by swapping: a sequence's blocks go to a pool in pinned host
+    memory, its device blocks are reused (poisoned here), and the blocks come
+    back into different physical blocks.  Decode is unchanged, bit for bit."""
+    print("swap out / swap in", flush=True)
+    dt, H, D = "bf16", 8, 128
+    d = W.make_decode(97, dt, H, D, [40, 700, 1500, 16, 333], spare=1.5)
+    t = {"q": up(d.q, dt), "kc": up(d.k_cache, dt), "vc": up(d.v_cache, dt),
+         "bt": up(d.block_tables), "cl": up(d.context_lens)}
+    def decode(tables):
+        out = torch.empty(d.q.shape, dtype=torch.float32, device="cuda")
+        ops.paged_attn_decode(t["q"], t["kc"], t["vc"], up(tables), t["cl"], d.scale, out,
+                              max_context_len=d.max_context_len)
+        return out
+    before = decode(d.block_tables)
+    victims = [1, 2, 4]
+    owned = [b for s in victims for b in d.block_tables[s, : -(-int(d.context_lens[s]) // 16)]]
+    host_k = torch.empty((len(owned) + 3,) + tuple(t["kc"].shape[1:]), dtype=torch.bfloat16, pin_memory=True)
+    host_v = torch.empty_like(host_k, pin_memory=True)
+    out_pairs = up(np.stack([owned, np.arange(len(owned))], axis=1).astype(np.int64))
+    ops.swap_blocks(t["kc"], t["vc"], host_k, host_v, out_pairs)
+    torch.cuda.synchronize()
+    assert np.array_equal(down(host_k)[: len(owned)], d.k_cache[owned])
+    assert np.array_equal(down(host_v)[: len(owned)], d.v_cache[owned])
+    # the freed device blocks are reused by someone else
+    idx = torch.as_tensor(owned, device="cuda")
+    t["kc"][idx] = float("nan"); t["vc"][idx] = float("nan")
+    # swap in to fresh physical blocks; the pair list itself lives in pinned host memory
+    in_use = set(d.block_tables.ravel().tolist())
+    fresh = [b for b in range(d.num_blocks) if b not in in_use][: len(owned)]
+    assert len(fresh) == len(owned)
+    in_pairs = torch.from_numpy(np.stack([np.arange(len(owned)), fresh], axis=1).astype(np.int64)).pin_memory()
+    ops.swap_blocks(host_k, host_v, t["kc"], t["vc"], in_pairs, device=torch.device("cuda", 0))
+    remap = dict(zip(owned, fresh))
+    tables = d.block_tables.copy()
+    for s in victims:
+        n = -(-int(d.context_lens[s]) // 16)
+        tables[s, :n] = [remap[b] for b in tables[s, :n]]
+    after = decode(tables)
+    assert torch.equal(before, after)
+    # pageable host memory is refused before any launch
+    import ctypes
+    from paged_kv_cache_137_amd import _lib
+    pageable = np.zeros(host_k.numel(), dtype=np.uint16)
+    desc = ops.cache_desc(t["kc"])
+    rc = _lib.lib().pkv_swap_blocks(ctypes.c_void_p(t["kc"].data_ptr()), ctypes.c_void_p(t["vc"].data_ptr()),
+                                    d.num_blocks, ctypes.c_void_p(pageable.ctypes.data),
+                                    ctypes.c_void_p(pageable.ctypes.data), host_k.shape[0], ctypes.byref(desc),
+                                    ctypes.c_void_p(out_pairs.data_ptr()), out_pairs.shape[0],
+                                    ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    assert rc == _lib.PKV_EINVAL
+    with pytest.raises(ValueError):
+        ops.swap_blocks(t["kc"], t["vc"], host_k.clone(), host_v.clone(), out_pairs)
