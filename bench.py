@@ -24,6 +24,11 @@ The same line also carries:
   sharing_step  parallel sampling over shared prompt blocks: the batched
                 copy-on-write copy, then decode (logical and unique KV GB/s).
   cached_prefix_prefill  requests prefilling over one cached shared prefix.
+  block_size_sweep  the same decode at 8-, 16- and 32-token blocks (the pool's
+                bytes re-tiled, fresh shuffled tables).
+  swap          swap-out/swap-in of 2048 blocks between the device pool and a
+                pinned host pool (pkv_swap_blocks), beside a plain contiguous
+                device<->host copy of the same bytes.
 """
 
 from __future__ import annotations
@@ -165,9 +170,14 @@ def main() -> int:
     for e in evs:
         step(e)
     torch.cuda.synchronize()
-    k_write = sum(e[0].elapsed_time(e[1]) for e in evs) / a.steps
-    k_dec = sum(e[1].elapsed_time(e[2]) for e in evs) / a.steps
-    k_red = sum(e[2].elapsed_time(e[3]) for e in evs) / a.steps
+    t_write = [e[0].elapsed_time(e[1]) for e in evs]
+    t_dec = [e[1].elapsed_time(e[2]) for e in evs]
+    t_red = [e[2].elapsed_time(e[3]) for e in evs]
+    k_write, k_dec, k_red = (sum(x) / a.steps for x in (t_write, t_dec, t_red))
+
+    def pct(x):
+        q = np.percentile(np.asarray(x), [10, 50, 90])
+        return [round(float(v), 5) for v in q]
 
     value = kv_bytes / (ms_step * 1e-3) / 1e9
     achieved = kv_bytes / (k_dec * 1e-3) / 1e9
@@ -197,14 +207,22 @@ def main() -> int:
         "head_tokens_attended_per_s": round(sum_ctx * H / (ms_step * 1e-3), 1),
         "kernels_ms": {"kv_cache_write": round(k_write, 5), "paged_decode_partial": round(k_dec, 5),
                        "paged_decode_reduce": round(k_red, 5)},
+        "kernels_ms_p10_p50_p90": {"kv_cache_write": pct(t_write), "paged_decode_partial": pct(t_dec),
+                                   "paged_decode_reduce": pct(t_red)},
         "roofline": {
-            "bound": "hbm", "kernel": "decode_partial_kernel<bf16,bf16,128>",
+            "bound": "hbm",
+            "kernel": "decode_plan_kernel + decode_partial_kernel<bf16,bf16,128,16> "
+                      "(one pkv_paged_attn_decode_partial call, bracketed by HIP events)",
+            "launch_ms": round(k_dec, 5),
             "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "algorithmic_bytes": kv_bytes,
             "traffic": None if traffic is None else int(traffic),
         },
     }
+    if not a.no_extras:
+        line["block_size_sweep"] = block_size_sweep(a, t, d)
+        line["swap"] = swap_step(a, t)
     del t, ws, out
     torch.cuda.empty_cache()
 
@@ -396,9 +414,99 @@ def cached_prefix_prefill(a, dev, up):
     }
 
 
-def cpu_baseline(d, seconds: float):
-    """The float64 oracle on whole sequences of the same step, one thread, until `seconds` pass."""
+def block_size_sweep(a, t, d):
+    """Decode of the headline batch at block sizes 8, 16 and 32.
+
+    The resident pool's bytes are re-tiled as [blocks][heads][B][dim] for each
+    B and every sequence gets freshly shuffled physical blocks, so the bytes
+    attended are the same and only the block granularity changes.
+    """
     import numpy as np
+    import torch
+
+    from paged_kv_cache_137_amd import ops
+
+    S, H, D = d.q.shape
+    ctx = d.context_lens.astype(np.int64)
+    kv_bytes = int(ctx.sum()) * 2 * H * D * 2
+    out = torch.empty((S, H, D), dtype=torch.bfloat16, device=t["q"].device)
+    res = {}
+    for B in (8, 16, 32):
+        nb = t["kc"].numel() // (H * B * D)
+        need = -(-ctx // B)
+        total = int(need.sum())
+        if total + 1 > nb:
+            res[str(B)] = None
+            continue
+        perm = np.random.default_rng(1000 + B).permutation(nb).astype(np.int32)
+        tables = np.full((S, int(need.max())), perm[total], dtype=np.int32)
+        offs = np.concatenate([[0], np.cumsum(need)])
+        for s_ in range(S):
+            tables[s_, : need[s_]] = perm[offs[s_]: offs[s_ + 1]]
+        kc = t["kc"].view(-1)[: nb * H * B * D].view(nb, H, B, D)
+        vc = t["vc"].view(-1)[: nb * H * B * D].view(nb, H, B, D)
+        bt = torch.from_numpy(tables).to(t["q"].device)
+        ws = torch.empty(ops.decode_workspace_bytes(S, H, D, d.max_context_len, a.partition), dtype=torch.uint8,
+                         device=t["q"].device)
+        ms = _time_events(lambda: ops.paged_attn_decode(t["q"], kc, vc, bt, t["cl"], d.scale, out,
+                                                        max_context_len=d.max_context_len,
+                                                        partition_size=a.partition, workspace=ws),
+                          a.warmup, a.steps)
+        res[str(B)] = {"decode_ms": round(ms, 4), "GBps": round(kv_bytes / (ms * 1e-3) / 1e9, 1),
+                       "frac": round(kv_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    return {"workload": "headline decode batch (partial + reduce), block sizes 8/16/32", "by_block_size": res}
+
+
+def swap_step(a, t, n_blocks: int = 2048):
+    """Swap-out and swap-in of n_blocks scattered 16-token blocks (keys and values)
+    between the device pool and a pinned host pool, beside a contiguous copy of
+    the same byte count (torch copy_, one DMA transfer) in each direction."""
+    import numpy as np
+    import torch
+
+    from paged_kv_cache_137_amd import ops
+
+    kc, vc = t["kc"], t["vc"]
+    nb = kc.shape[0]
+    dev = kc.device
+    ids = np.random.default_rng(7).permutation(nb)[:n_blocks].astype(np.int64)
+    hk = torch.empty((n_blocks,) + tuple(kc.shape[1:]), dtype=kc.dtype, pin_memory=True)
+    hv = torch.empty_like(hk, pin_memory=True)
+    out_pairs = torch.from_numpy(np.stack([ids, np.arange(n_blocks)], axis=1)).to(dev)
+    in_pairs = torch.from_numpy(np.stack([np.arange(n_blocks), ids], axis=1)).to(dev)
+    nbytes = 2 * hk.numel() * hk.element_size()
+    steps, warm = max(3, a.steps // 10), 2
+    out_ms = _time_events(lambda: ops.swap_blocks(kc, vc, hk, hv, out_pairs), warm, steps)
+    in_ms = _time_events(lambda: ops.swap_blocks(hk, hv, kc, vc, in_pairs, device=dev), warm, steps)
+    dk = torch.empty((2,) + tuple(hk.shape), dtype=kc.dtype, device=dev)
+    hd = torch.empty(tuple(dk.shape), dtype=kc.dtype, pin_memory=True)
+    d2h_ms = _time_events(lambda: hd.copy_(dk, non_blocking=True), warm, steps)
+    h2d_ms = _time_events(lambda: dk.copy_(hd, non_blocking=True), warm, steps)
+    gbps = lambda ms: round(nbytes / (ms * 1e-3) / 1e9, 1)  # noqa: E731
+    return {
+        "workload": f"{n_blocks} scattered blocks x (keys + values), 32 heads x 16 x 128 bf16 "
+                    f"({nbytes / 2**20:.0f} MiB per direction)",
+        "swap_out_ms": round(out_ms, 3), "swap_out_GBps": gbps(out_ms),
+        "swap_in_ms": round(in_ms, 3), "swap_in_GBps": gbps(in_ms),
+        "contiguous_d2h_GBps": gbps(d2h_ms), "contiguous_h2d_GBps": gbps(h2d_ms),
+    }
+
+
+def _cpu_model() -> str:
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(d, seconds: float):
+    """The float64 oracle on whole sequences of the same step, one thread.
+
+    Sequences are taken in order, wrapping round to the first again, until
+    `seconds` have passed; the rate is K/V bytes attended per second."""
     import threadpoolctl
 
     import oracle
@@ -407,10 +515,11 @@ def cpu_baseline(d, seconds: float):
     done, tokens = 0, 0
     with threadpoolctl.threadpool_limits(1):
         t0 = time.perf_counter()
-        while done < d.num_seqs and (time.perf_counter() - t0) < seconds:
+        while (time.perf_counter() - t0) < seconds:
+            s_ = done % d.num_seqs
             oracle.attention.paged_decode(d.q, d.k_cache, d.v_cache, d.block_tables, d.context_lens, d.scale,
-                                          d.dtype, seqs=[done])
-            tokens += int(d.context_lens[done])
+                                          d.dtype, seqs=[s_])
+            tokens += int(d.context_lens[s_])
             done += 1
         el = time.perf_counter() - t0
     return {
@@ -419,8 +528,9 @@ def cpu_baseline(d, seconds: float):
         "cores": 1,
         "kind": "oracle",
         "tokens_attended_per_s": round(tokens / el, 1),
-        "sample": f"first {done} of {d.num_seqs} sequences of the same decode step ({tokens} tokens, "
-                  f"{el:.1f} s), float64 NumPy, BLAS limited to 1 thread",
+        "cpu_model": _cpu_model(),
+        "sample": f"{done} whole-sequence decodes from the same step's {d.num_seqs} sequences, in order and "
+                  f"wrapping round ({tokens} tokens, {el:.1f} s), float64 NumPy, BLAS limited to 1 thread",
     }
 
 
