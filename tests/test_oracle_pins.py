@@ -461,3 +461,148 @@ def test_prefix_prefill_reduces_to_causal_and_to_decode():
     assert np.abs(got[-1] - dec[0]).max() < 1e-13
     first = _sdpa(qn[0][:, None, :], K[:, : C + 1].copy(), V[:, : C + 1].copy(), 0.5)[:, 0, :]
     assert np.abs(got[0] - first).max() < 1e-13
+
+
+def test_block_count_invariants():
+    # Closed forms every block size must satisfy (P1 section 4.2; P3 section III):
+    # the blocks hold the tokens with less than one block to spare, and the last
+    # block is full exactly when the length is a multiple of the block size.
+    for B in (1, 4, 8, 16, 32):
+        for n in range(0, 130):
+            nb, w = BK.blocks_needed(n, B), BK.wasted_slots(n, B)
+            assert nb * B - w == n and 0 <= w < B
+            assert (w == 0) == (n % B == 0)
+            f = BK.filled_counts(n, B)
+            assert len(f) == nb and sum(f) == n and all(0 < x <= B for x in f)
+            assert all(x == B for x in f[:-1])
+            if n:
+                r = BK.block_token_ranges(n, B)
+                assert r[0][0] == 1 and r[-1][1] == n
+                assert all(b[0] == a[1] + 1 for a, b in zip(r, r[1:]))
+
+
+# Planted mistakes in the bookkeeping, the cache write and the block copies, and
+# the cached-prefix prefill: each must break at least one of the pins below.
+_OTHER_PINS = (
+    test_kv_bytes_per_token_opt13b, test_request_300_blocks_and_waste, test_query_40_block_ranges,
+    test_block_table_figure, test_figure6_walkthrough, test_max_kv_slots_13b, test_slot_mapping_matches_slot_of,
+    test_block_count_invariants, test_cache_write_then_gather_returns_inputs,
+    test_copy_blocks_duplicates_whole_blocks_only, test_prefix_prefill_reduces_to_causal_and_to_decode,
+)
+
+
+def _other_pins_pass():
+    for pin in _OTHER_PINS:
+        try:
+            with np.errstate(all="ignore"):
+                pin()
+        except (AssertionError, IndexError, ValueError):
+            return False
+    return True
+
+
+def _other_mutants():
+    real_write, real_copy = A.cache_write, A.copy_blocks
+
+    def bn_floor(n, B):
+        return n // B
+
+    def waste_full_block(n, B):
+        return B - n % B
+
+    def ranges_zero_based(i, B):
+        return [(j * B, min((j + 1) * B, i) - 1) for j in range(-(-i // B))]
+
+    def filled_first_partial(n, B):
+        f = [min(B, n - j * B) for j in range(-(-n // B))]
+        return f[::-1]
+
+    def slot_no_scale(table, pos, B):
+        return int(table[pos // B]) + pos % B
+
+    def slot_offset_flipped(table, pos, B):
+        return int(table[pos // B]) * B + (B - 1 - pos % B)
+
+    def kv_bytes_no_pair(hidden, layers, b):
+        return hidden * layers * b
+
+    def write_k_into_v(k_cache, v_cache, k, v, slots, B):
+        return real_write(k_cache, v_cache, k, k, slots, B)
+
+    def write_negative_wraps(k_cache, v_cache, k, v, slots, B):
+        s = np.asarray(slots, dtype=np.int64) % (k_cache.shape[0] * B)
+        return real_write(k_cache, v_cache, k, v, s, B)
+
+    def write_block_offset_swapped(k_cache, v_cache, k, v, slots, B):
+        kc, vc = k_cache.copy(), v_cache.copy()
+        for t, s in enumerate(np.asarray(slots, dtype=np.int64)):
+            if s >= 0:
+                kc[s // B, :, (s % B + 1) % B, :] = k[t]
+                vc[s // B, :, (s % B + 1) % B, :] = v[t]
+        return kc, vc
+
+    def copy_keys_only(k_cache, v_cache, pairs):
+        nk, _ = real_copy(k_cache, v_cache, pairs)
+        return nk, v_cache.copy()
+
+    def copy_reversed(k_cache, v_cache, pairs):
+        return real_copy(k_cache, v_cache, [(d, s) for s, d in np.asarray(pairs).reshape(-1, 2)])
+
+    def prefix_ignored(q, k_cache, v_cache, tables, prefix_lens, prompt_lens, scale, dtype, block_size=16,
+                       prompts=None):
+        T, H, D = q.shape
+        out = np.full((T, H, D), np.nan)
+        offs = np.concatenate([[0], np.cumsum(np.asarray(prompt_lens, dtype=np.int64))])
+        for p in range(len(prompt_lens)):
+            C, L = int(prefix_lens[p]), int(prompt_lens[p])
+            K = A.to_f64(A.gather(k_cache, tables[p], C + L, block_size), dtype)[:, C:]
+            V = A.to_f64(A.gather(v_cache, tables[p], C + L, block_size), dtype)[:, C:]
+            Q = A.to_f64(q[offs[p]: offs[p + 1]], dtype)
+            for i in range(L):
+                for h in range(H):
+                    out[offs[p] + i, h] = A.attend(Q[i, h], K[h, : i + 1], V[h, : i + 1], scale)
+        return out
+
+    def prefix_excludes_self(q, k_cache, v_cache, tables, prefix_lens, prompt_lens, scale, dtype, block_size=16,
+                             prompts=None):
+        T, H, D = q.shape
+        out = np.full((T, H, D), np.nan)
+        offs = np.concatenate([[0], np.cumsum(np.asarray(prompt_lens, dtype=np.int64))])
+        for p in range(len(prompt_lens)):
+            C, L = int(prefix_lens[p]), int(prompt_lens[p])
+            K = A.to_f64(A.gather(k_cache, tables[p], C + L, block_size), dtype)
+            V = A.to_f64(A.gather(v_cache, tables[p], C + L, block_size), dtype)
+            Q = A.to_f64(q[offs[p]: offs[p + 1]], dtype)
+            for i in range(L):
+                n = max(C + i, 1)
+                for h in range(H):
+                    out[offs[p] + i, h] = A.attend(Q[i, h], K[h, :n], V[h, :n], scale)
+        return out
+
+    return {
+        "blocks rounded down": (BK, "blocks_needed", bn_floor),
+        "waste of a full last block is a block": (BK, "wasted_slots", waste_full_block),
+        "ranges counted from 0": (BK, "block_token_ranges", ranges_zero_based),
+        "partial block first": (BK, "filled_counts", filled_first_partial),
+        "slot misses the block size": (BK, "slot_of", slot_no_scale),
+        "slot offset flipped": (BK, "slot_of", slot_offset_flipped),
+        "key or value missing from KV bytes": (BK, "kv_bytes_per_token", kv_bytes_no_pair),
+        "write puts keys into values": (A, "cache_write", write_k_into_v),
+        "negative slot wraps round": (A, "cache_write", write_negative_wraps),
+        "write offset shifted": (A, "cache_write", write_block_offset_swapped),
+        "copy moves keys only": (A, "copy_blocks", copy_keys_only),
+        "copy direction reversed": (A, "copy_blocks", copy_reversed),
+        "prefix ignored": (A, "prefix_prefill", prefix_ignored),
+        "new token does not see itself": (A, "prefix_prefill", prefix_excludes_self),
+    }
+
+
+@pytest.mark.parametrize("name", sorted(_other_mutants()))
+def test_planted_mistake_in_bookkeeping_copies_or_prefix_is_caught(name, monkeypatch):
+    mod, attr, fn = _other_mutants()[name]
+    monkeypatch.setattr(mod, attr, fn)
+    assert not _other_pins_pass(), f"no pin catches: {name}"
+
+
+def test_unmutated_bookkeeping_copies_and_prefix_pass_all_pins():
+    assert _other_pins_pass()
