@@ -9,16 +9,18 @@
 // all blocks so far).
 //
 // Work decomposition (designed for CDNA4, not taken from the pages):
-//  - A unit of work is one (sequence, head, context partition).  A plan kernel
-//    (one workgroup) lists the (sequence, partition) pairs that hold tokens.
-//    It sorts them by size, largest first, with a counting sort, and resets a
-//    work counter.  The decode kernel is persistent.  Just enough 4-wave
-//    workgroups to fill the GPU claim units from the counter until none are
-//    left.  Empty partitions cost nothing, and the ragged tail is spread over
-//    the whole GPU.  No output depends on which workgroup ran which unit, so
-//    results are deterministic.
-//  - Inside a unit, wave w takes the partition's blocks w, w+4, w+8, ..., so a
-//    short partition still spreads over all waves.
+//  - A unit of work is one (sequence, context partition) for NW consecutive
+//    heads.  A plan kernel (one workgroup) lists the (sequence, partition)
+//    pairs that hold tokens.  It sorts them by size, largest first, with a
+//    counting sort, and resets a work counter.  The decode kernel is
+//    persistent.  Just enough NW-wave workgroups to fill the GPU claim units
+//    from the counter until none are left.  Empty partitions cost nothing, and
+//    the ragged tail is spread over the whole GPU.  No output depends on which
+//    workgroup ran which unit, so results are deterministic.
+//  - Inside a unit, wave w takes head NW*g + w alone and streams all of the
+//    partition's blocks for it.  A claim, the metadata lookups and the start of
+//    the load pipeline are thus shared by NW heads, and the waves of a
+//    workgroup, having equal block counts, stay in step between claims.
 //  - A (block, head) tile is BS tokens x D values stored contiguously (BS = 16
 //    by default; 8 and 32 are built too).  A wave
 //    reads it with NI 16-byte loads per lane, each load instruction covering
@@ -31,7 +33,8 @@
 //    lane of the row ends with the same score.
 //  - Online softmax per token row: each lane row keeps its own running max,
 //    sum and VEC accumulators, so the steady state needs no cross-row traffic.
-//    Rows and waves are merged once per unit, through LDS.
+//    The rows are merged once per unit with cross-lane shuffles, in a fixed
+//    butterfly order; no LDS is used.
 //  - Software pipelining: the next block's K/V loads are issued before the
 //    current block is consumed (ping-pong register sets, no branch between
 //    them), so two tiles per wave are in flight.
@@ -149,40 +152,36 @@ __global__ __launch_bounds__(NW * 64) void decode_partial_kernel(const DecodeArg
   using G = DecodeGeom<E, D, BS>;
   using C = Chunk<E>;
   constexpr int VEC = G::VEC, LPT = G::LPT, TPI = G::TPI, NI = G::NI;
-  constexpr int ROWS = NW * TPI;  // online-softmax states per workgroup
 
-  __shared__ float sm_m[ROWS];
-  __shared__ float sm_l[ROWS];
-  __shared__ __attribute__((aligned(16))) float sm_acc[ROWS][D];
   __shared__ int sm_unit[2];
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane / LPT;
   const int c = lane % LPT;
+  const int H = a.num_heads;
+  const int HG = (H + NW - 1) / NW;  // head groups
   const int part_tokens = a.part_blocks * BS;
-  const int total = a.work_ctrl[1] * a.num_heads;
-  const int64_t bstride = (int64_t)a.num_heads * G::TILE;
+  const int total = a.work_ctrl[1] * HG;
+  const int64_t bstride = (int64_t)H * G::TILE;
 
   for (int it = 0;; ++it) {
-    // Claim the next unit.  The slot alternates with the iteration, so one
-    // barrier suffices: a slot is rewritten only after every wave has passed
-    // the following iteration's barrier.
+    // Claim the next unit; the slot alternates so one barrier suffices.
     if (threadIdx.x == 0) sm_unit[it & 1] = atomicAdd(&a.work_ctrl[0], 1);
     __syncthreads();
     const int u = __builtin_amdgcn_readfirstlane(sm_unit[it & 1]);
     if (u >= total) break;
-    const int e = u / a.num_heads;
-    const int h = u - e * a.num_heads;
+    const int e = u / HG;
+    const int h = (u - e * HG) * NW + w;
+    if (h >= H) continue;  // a partial last head group
     const int entry = a.work_list[e];
     const int s = entry / a.num_parts;
     const int p = entry - s * a.num_parts;
-
-    const int64_t sh = (int64_t)s * a.num_heads + h;
+    const int64_t sh = (int64_t)s * H + h;
     const int ctx = clamp_ctx(a, s);
     const int tok0 = p * part_tokens;
     if (ctx <= 0) {  // undefined attention: report NaN rather than garbage
-      if (threadIdx.x < D) Out<O>::put(a.out, sh * D + threadIdx.x, __builtin_nanf(""));
+      for (int t = lane; t < D; t += 64) Out<O>::put(a.out, sh * D + t, __builtin_nanf(""));
       continue;
     }
     if (tok0 >= ctx) continue;
@@ -253,69 +252,63 @@ __global__ __launch_bounds__(NW * 64) void decode_partial_kernel(const DecodeArg
         bad = (uint64_t)(uint32_t)ph >= (uint64_t)a.num_blocks;
         return bad ? 0 : ph;
       };
-      int j = w;
-      if (j >= cn) continue;
+      int j = 0;
       if constexpr (G::PINGPONG) {
-      uint4 kA[NI], vA[NI], kB[NI], vB[NI];
-      bool badA, badB;
-      load(phys_of(j, badA), kA, vA);
-      while (j + 2 * NW < cn) {
-        load(phys_of(j + NW, badB), kB, vB);
-        consume(kA, vA, cb + j, badA);
-        load(phys_of(j + 2 * NW, badA), kA, vA);
-        consume(kB, vB, cb + j + NW, badB);
-        j += 2 * NW;
-      }
-      if (j + NW < cn) {
-        load(phys_of(j + NW, badB), kB, vB);
-        consume(kA, vA, cb + j, badA);
-        consume(kB, vB, cb + j + NW, badB);
-      } else {
-        consume(kA, vA, cb + j, badA);
-      }
-      } else {
-      for (; j < cn; j += NW) {
-        uint4 kA[NI], vA[NI];
-        bool badA;
+        uint4 kA[NI], vA[NI], kB[NI], vB[NI];
+        bool badA, badB;
         load(phys_of(j, badA), kA, vA);
-        consume(kA, vA, cb + j, badA);
-      }
-      }
-    }
-
-    // Merge the ROWS running states of this unit: max, rescaled sums.
-    if (c == 0) {
-      sm_m[w * TPI + r] = m;
-      sm_l[w * TPI + r] = l;
-    }
-#pragma unroll
-    for (int e2 = 0; e2 < VEC; ++e2) sm_acc[w * TPI + r][c * VEC + e2] = acc[e2];
-    __syncthreads();
-    if (threadIdx.x < D) {
-      const int t = threadIdx.x;
-      float M = sm_m[0];
-#pragma unroll
-      for (int k = 1; k < ROWS; ++k) M = fmaxf(M, sm_m[k]);
-      float Ls = 0.f, A = 0.f;
-#pragma unroll
-      for (int k = 0; k < ROWS; ++k) {
-        const float f = fast_exp2(sm_m[k] - M);
-        Ls = fmaf(sm_l[k], f, Ls);
-        A = fmaf(sm_acc[k][t], f, A);
-      }
-      if (nparts == 1) {
-        Out<O>::put(a.out, sh * D + t, A / Ls);
+        while (j + 2 < cn) {
+          load(phys_of(j + 1, badB), kB, vB);
+          consume(kA, vA, cb + j, badA);
+          load(phys_of(j + 2, badA), kA, vA);
+          consume(kB, vB, cb + j + 1, badB);
+          j += 2;
+        }
+        if (j + 1 < cn) {
+          load(phys_of(j + 1, badB), kB, vB);
+          consume(kA, vA, cb + j, badA);
+          consume(kB, vB, cb + j + 1, badB);
+        } else {
+          consume(kA, vA, cb + j, badA);
+        }
       } else {
-        const int64_t pi = sh * a.num_parts + p;
-        a.ws_acc[pi * D + t] = A;
-        if (t == 0) {
-          a.ws_ml[pi * 2] = M;
-          a.ws_ml[pi * 2 + 1] = Ls;
+        for (; j < cn; ++j) {
+          uint4 kA[NI], vA[NI];
+          bool badA;
+          load(phys_of(j, badA), kA, vA);
+          consume(kA, vA, cb + j, badA);
         }
       }
     }
-    // The next unit's LDS writes come after the next claim barrier, which every
-    // thread reaches only after finishing the merge above.
+
+    // Merge the wave's TPI token rows (lanes c, c + LPT, ... hold the same
+    // dims): common maximum, rescaled sums, in a fixed butterfly order.
+    float M = m;
+#pragma unroll
+    for (int sft = LPT; sft < 64; sft <<= 1) M = fmaxf(M, __shfl_xor(M, sft, 64));
+    const float f = fast_exp2(m - M);
+    float Ls = l * f;
+#pragma unroll
+    for (int e2 = 0; e2 < VEC; ++e2) acc[e2] *= f;
+#pragma unroll
+    for (int sft = LPT; sft < 64; sft <<= 1) {
+      Ls += __shfl_xor(Ls, sft, 64);
+#pragma unroll
+      for (int e2 = 0; e2 < VEC; ++e2) acc[e2] += __shfl_xor(acc[e2], sft, 64);
+    }
+    if (r == 0) {
+      if (nparts == 1) {
+#pragma unroll
+        for (int e2 = 0; e2 < VEC; ++e2) Out<O>::put(a.out, sh * D + c * VEC + e2, acc[e2] / Ls);
+      } else {
+        const int64_t pi = sh * a.num_parts + p;
+        float* dst = a.ws_acc + pi * D + c * VEC;
+#pragma unroll
+        for (int e2 = 0; e2 < VEC; e2 += 4)
+          *reinterpret_cast<float4*>(dst + e2) = make_float4(acc[e2], acc[e2 + 1], acc[e2 + 2], acc[e2 + 3]);
+        if (c == 0) *reinterpret_cast<float2*>(a.ws_ml + pi * 2) = make_float2(M, Ls);
+      }
+    }
   }
 }
 
@@ -367,7 +360,7 @@ static int persistent_grid(K kernel, int block, int64_t units) {
 template <typename E, typename O, int D, int BS>
 static hipError_t partial_bs(const DecodeArgs& a, hipStream_t st) {
   hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(1024), 0, st, a);
-  const int grid = persistent_grid(decode_partial_kernel<E, O, D, BS>, NW * 64, a.total_units);
+  const int grid = persistent_grid(decode_partial_kernel<E, O, D, BS>, NW * 64, ((int64_t)a.total_units + NW - 1) / NW);
   hipLaunchKernelGGL((decode_partial_kernel<E, O, D, BS>), dim3(grid), dim3(NW * 64), 0, st, a);
   return hipGetLastError();
 }

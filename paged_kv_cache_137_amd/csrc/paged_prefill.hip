@@ -55,6 +55,9 @@ namespace pkv {
 #define PKV_PRE_XCD 1
 #endif
 
+// Buffer resource word 3 for gfx9-family parts: raw (untyped) 32-bit dword access.
+constexpr int BUF_RSRC_WORD3 = 0x00020000;
+
 template <typename E>
 __device__ __forceinline__ f32x16_t mfma32(const uint4& a, const uint4& b, const f32x16_t& c);
 template <>
@@ -170,6 +173,11 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
   for (int i = lane; i < pr; i += 64) off += max(a.prompt_lens[i], 0);
 #pragma unroll
   for (int sft = 32; sft >= 1; sft >>= 1) off += __shfl_xor(off, sft, 64);
+  // Every lane holds the same sum; make that visible to the compiler, so that
+  // the buffer descriptors built from it live in scalar registers.
+  if constexpr (!PAGED)
+    off = (long long)(((unsigned long long)(uint32_t)__builtin_amdgcn_readfirstlane((int)(off >> 32)) << 32) |
+                      (uint32_t)__builtin_amdgcn_readfirstlane((int)off));
   if (off + L > a.total_tokens) L = (int)max(0ll, (long long)a.total_tokens - off);
   // C: cached prefix tokens ahead of the new ones; keys are indexed by absolute
   // position 0 .. C+L-1, and new token i sits at position C + i.
@@ -252,14 +260,22 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
     } else {
       const char* kt = kb + (int64_t)n0 * rsb;
       const char* vt = vb + (int64_t)n0 * rsb;
+      // Buffer loads over exactly this tile's rows that exist: a row at or past
+      // the prompt end lies at or beyond num_records, so the hardware returns
+      // zeros for it.  (Row r of the tile starts at r * rsb; the last existing
+      // row ends at (rows - 1) * rsb + 2 * D, and rsb >= 2 * D.)  Offsets stay
+      // below 64 * rsb <= 64 * 65535 * 128 * 2 < 2^31 under the ABI's limits.
+      const int rows = min(L - n0, BN);  // >= 1: n0 < L here
+      const int nrec = (rows - 1) * (int)rsb + D * 2;
+      const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)kt, (short)0, nrec, BUF_RSRC_WORD3);
+      const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)vt, (short)0, nrec, BUF_RSRC_WORD3);
 #pragma unroll
       for (int i = 0; i < KCH; ++i)
-        kst[i] = n0 + krow[i] < L ? *reinterpret_cast<const uint4*>(kt + koff[i]) : make_uint4(0u, 0u, 0u, 0u);
+        kst[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, (int)koff[i], 0, 0));
       if (threadIdx.x < VG) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          vst[i] = n0 + 4 * vg + i < L ? *reinterpret_cast<const uint4*>(vt + voff + i * rsb)
-                                       : make_uint4(0u, 0u, 0u, 0u);
+          vst[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, (int)(voff + i * rsb), 0, 0));
       }
     }
   };
