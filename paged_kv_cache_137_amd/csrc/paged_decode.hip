@@ -27,7 +27,10 @@
 //    1 KiB of consecutive bytes.  Lane l holds dims (l % LPT)*VEC .. +VEC of
 //    token row l / LPT.  K/V are read with the nontemporal hint: every tile is
 //    used once per unit, and keeping it out of the cache hierarchy's
-//    retention raises the sustained HBM rate.
+//    retention raises the sustained HBM rate.  Partitions whose blocks the
+//    plan kernel finds shared with a neighbouring sequence (parallel samples,
+//    a common prefix) are read with cached loads instead, so that the other
+//    sequences' reads of the same blocks hit in L2.
 //  - q.k: packed dot products (v_dot2 for 16-bit inputs) over the lane's VEC
 //    dims, then a DPP butterfly across the LPT lanes of the token row.  Every
 //    lane of the row ends with the same score.
@@ -40,6 +43,8 @@
 //    them), so two tiles per wave are in flight.
 //  - Masking of slots at or past the context length is a select (-inf score,
 //    zeroed V), never a multiply, so stale NaN data in those slots cannot leak.
+#include <type_traits>
+
 #include "pkv_device.h"
 #include "pkv_internal.h"
 
@@ -60,12 +65,12 @@ constexpr int PLAN_BUCKETS = 257;  // partition sizes 0..256 blocks (larger ones
 
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
+template <bool NT>
 __device__ __forceinline__ uint4 load_kv16(const char* p) {
-#if PKV_DEC_NT
-  return __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p)));
-#else
-  return *reinterpret_cast<const uint4*>(p);
-#endif
+  if constexpr (NT && PKV_DEC_NT)
+    return __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p)));
+  else
+    return *reinterpret_cast<const uint4*>(p);
 }
 
 template <typename E, int D, int BS>
@@ -136,13 +141,25 @@ __global__ __launch_bounds__(1024) void decode_plan_kernel(const DecodeArgs a) {
   for (int s = threadIdx.x; s < a.num_seqs; s += blockDim.x) {
     const int ctx = clamp_ctx(a, s);
     if (ctx <= 0) {
-      a.work_list[atomicAdd(&cnt[0], 1)] = s * a.num_parts;
+      a.work_list[atomicAdd(&cnt[0], 1)] = (s * a.num_parts) << 1;
       continue;
     }
+    const int32_t* row = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
     int p = 0;
     for (int t0 = 0; t0 < ctx; t0 += part_tokens, ++p) {
       const int nb = (min(part_tokens, ctx - t0) + BS - 1) / BS;
-      a.work_list[atomicAdd(&cnt[min(nb, PLAN_BUCKETS - 1)], 1)] = s * a.num_parts + p;
+      // Shared blocks (parallel samples, a common prefix) are read by several
+      // sequences close together in time; those partitions are read with
+      // cached loads so that the repeats hit in L2.  The sign of sharing used:
+      // a neighbouring sequence holds the same physical block at the
+      // partition's first logical position.
+      const int lb = p * a.part_blocks;
+      const int mine = row[lb];
+      int shared = 0;
+      for (int s2 = max(s - 1, 0); s2 <= min(s + 1, a.num_seqs - 1); ++s2)
+        if (s2 != s && clamp_ctx(a, s2) > lb * BS && a.block_tables[(int64_t)s2 * a.max_blocks_per_seq + lb] == mine)
+          shared = 1;
+      a.work_list[atomicAdd(&cnt[min(nb, PLAN_BUCKETS - 1)], 1)] = ((s * a.num_parts + p) << 1) | shared;
     }
   }
 }
@@ -174,7 +191,9 @@ __global__ __launch_bounds__(NW * 64) void decode_partial_kernel(const DecodeArg
     const int e = u / HG;
     const int h = (u - e * HG) * NW + w;
     if (h >= H) continue;  // a partial last head group
-    const int entry = a.work_list[e];
+    const int tagged = a.work_list[e];
+    const bool reuse = tagged & 1;  // blocks shared with a neighbouring sequence
+    const int entry = tagged >> 1;
     const int s = entry / a.num_parts;
     const int p = entry - s * a.num_parts;
     const int64_t sh = (int64_t)s * H + h;
@@ -198,14 +217,6 @@ __global__ __launch_bounds__(NW * 64) void decode_partial_kernel(const DecodeArg
 #pragma unroll
     for (int e2 = 0; e2 < VEC; ++e2) acc[e2] = 0.f;
 
-    auto load = [&](int phys, uint4 (&kx)[NI], uint4 (&vx)[NI]) {
-      const char* kp = kbase + (int64_t)phys * bstride;
-      const char* vp = vbase + (int64_t)phys * bstride;
-#pragma unroll
-      for (int i = 0; i < NI; ++i) kx[i] = load_kv16(kp + i * 1024);
-#pragma unroll
-      for (int i = 0; i < NI; ++i) vx[i] = load_kv16(vp + i * 1024);
-    };
 
     auto consume = [&](const uint4 (&kx)[NI], uint4 (&vx)[NI], int jb, bool bad) {
       const int tb = tok0 + jb * BS;  // position of the block's first token
@@ -243,43 +254,58 @@ __global__ __launch_bounds__(NW * 64) void decode_partial_kernel(const DecodeArg
       }
     };
 
-    for (int cb = 0; cb < nblk; cb += 64) {
-      const int cn = min(64, nblk - cb);
-      // The chunk's table entries, one per lane; a wave-uniform readlane picks each.
-      const int tv = lane < cn ? trow[cb + lane] : 0;
-      auto phys_of = [&](int j, bool& bad) {
-        const int ph = __builtin_amdgcn_readlane(tv, j);
-        bad = (uint64_t)(uint32_t)ph >= (uint64_t)a.num_blocks;
-        return bad ? 0 : ph;
+    // The whole stream is instantiated once per load kind, so that the choice
+    // is made once per unit and the loop bodies stay straight-line.
+    auto run = [&](auto nt_c) {
+      constexpr bool NTL = decltype(nt_c)::value;
+      auto load = [&](int phys, uint4 (&kx)[NI], uint4 (&vx)[NI]) {
+        const char* kp = kbase + (int64_t)phys * bstride;
+        const char* vp = vbase + (int64_t)phys * bstride;
+#pragma unroll
+        for (int i = 0; i < NI; ++i) kx[i] = load_kv16<NTL>(kp + i * 1024);
+#pragma unroll
+        for (int i = 0; i < NI; ++i) vx[i] = load_kv16<NTL>(vp + i * 1024);
       };
-      int j = 0;
-      if constexpr (G::PINGPONG) {
-        uint4 kA[NI], vA[NI], kB[NI], vB[NI];
-        bool badA, badB;
-        load(phys_of(j, badA), kA, vA);
-        while (j + 2 < cn) {
-          load(phys_of(j + 1, badB), kB, vB);
-          consume(kA, vA, cb + j, badA);
-          load(phys_of(j + 2, badA), kA, vA);
-          consume(kB, vB, cb + j + 1, badB);
-          j += 2;
-        }
-        if (j + 1 < cn) {
-          load(phys_of(j + 1, badB), kB, vB);
-          consume(kA, vA, cb + j, badA);
-          consume(kB, vB, cb + j + 1, badB);
-        } else {
-          consume(kA, vA, cb + j, badA);
-        }
-      } else {
-        for (; j < cn; ++j) {
-          uint4 kA[NI], vA[NI];
-          bool badA;
+      for (int cb = 0; cb < nblk; cb += 64) {
+        const int cn = min(64, nblk - cb);
+        // The chunk's table entries, one per lane; a wave-uniform readlane picks each.
+        const int tv = lane < cn ? trow[cb + lane] : 0;
+        auto phys_of = [&](int j, bool& bad) {
+          const int ph = __builtin_amdgcn_readlane(tv, j);
+          bad = (uint64_t)(uint32_t)ph >= (uint64_t)a.num_blocks;
+          return bad ? 0 : ph;
+        };
+        int j = 0;
+        if constexpr (G::PINGPONG) {
+          uint4 kA[NI], vA[NI], kB[NI], vB[NI];
+          bool badA, badB;
           load(phys_of(j, badA), kA, vA);
-          consume(kA, vA, cb + j, badA);
+          while (j + 2 < cn) {
+            load(phys_of(j + 1, badB), kB, vB);
+            consume(kA, vA, cb + j, badA);
+            load(phys_of(j + 2, badA), kA, vA);
+            consume(kB, vB, cb + j + 1, badB);
+            j += 2;
+          }
+          if (j + 1 < cn) {
+            load(phys_of(j + 1, badB), kB, vB);
+            consume(kA, vA, cb + j, badA);
+            consume(kB, vB, cb + j + 1, badB);
+          } else {
+            consume(kA, vA, cb + j, badA);
+          }
+        } else {
+          for (; j < cn; ++j) {
+            uint4 kA[NI], vA[NI];
+            bool badA;
+            load(phys_of(j, badA), kA, vA);
+            consume(kA, vA, cb + j, badA);
+          }
         }
       }
-    }
+    };
+    if (reuse) run(std::false_type{});
+    else run(std::true_type{});
 
     // Merge the wave's TPI token rows (lanes c, c + LPT, ... hold the same
     // dims): common maximum, rescaled sums, in a fixed butterfly order.

@@ -116,6 +116,7 @@ int decode_impl(int stages, const void* q, const void* k_cache, const void* v_ca
       plan_decode(num_seqs, desc->num_heads, desc->head_dim, max_context_len, partition_size, bsz);
   const int64_t units = (int64_t)num_seqs * desc->num_heads * plan.num_parts;
   if (units > ((int64_t)1 << 31) - 64 || num_seqs > 65535 * 32768) return PKV_EINVAL;
+  if ((int64_t)num_seqs * plan.num_parts >= ((int64_t)1 << 30)) return PKV_EINVAL;  // work-list entries carry a tag bit
   if (desc->num_heads > 65535) return PKV_EINVAL;
   if (workspace == nullptr || !aligned(workspace, 16)) return PKV_EINVAL;
   if (workspace_bytes < plan.ws_bytes) return PKV_EWORKSPACE;
