@@ -315,33 +315,36 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
   const int kend = C + min(L, m0 + BM);     // keys any query of the workgroup sees
   const int wkend = C + min(L, qrow0 + 32); // keys any query of this wave sees
 
-  // One 64-key tile from LDS buffer `buf`, starting at key n0, as NSUB (1 or 2)
-  // sub-tiles of 32 keys.  The sub-tiles' score chains are independent, so
-  // their MFMAs interleave.  Lane (ql, hf) score element j of sub-tile u is key
-  // n0 + 32u + 8*(j/4) + 4*hf + j%4 against query qi.
+  // One 64-key tile from LDS buffer `buf`, starting at key n0, as two
+  // sub-tiles of 32 keys whose score chains are independent, so their MFMAs
+  // interleave.  Lane (ql, hf) score element j of sub-tile u is key
+  // n0 + 32u + 8*(j/4) + 4*hf + j%4 against query qi.  MASKED tiles select
+  // -inf for every key past the query (or past the prompt end).  Every tile
+  // body is one instantiation per MASKED value, so the accumulators stay in
+  // place across iterations.
   //
   // The two half-waves hold different keys of the same queries.  Each keeps a
   // lane-local partial row sum against a shared reference maximum mrow.  They
   // exchange values only when mrow must move: when some row's maximum rises by
   // more than the slack.
-  auto tile = [&](auto nsub_c, int buf, int n0) {
-    constexpr int NSUB = decltype(nsub_c)::value;
-    f32x16_t st[NSUB];
+  auto tile = [&](auto masked_c, int buf, int n0) {
+    constexpr bool MASKED = decltype(masked_c)::value;
+    f32x16_t st[2];
 #pragma unroll
-    for (int u = 0; u < NSUB; ++u)
+    for (int u = 0; u < 2; ++u)
 #pragma unroll
       for (int j = 0; j < 16; ++j) st[u][j] = 0.f;
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk)
 #pragma unroll
-      for (int u = 0; u < NSUB; ++u) {
+      for (int u = 0; u < 2; ++u) {
         const unsigned char* kr = k_lds[buf] + (u * 32 + ql) * KROW + hf * 16;
         st[u] = mfma32<E>(*reinterpret_cast<const uint4*>(kr + kk * 32), qf[kk], st[u]);
       }
 
-    if ((n0 + 32 * NSUB - 1 > C + qrow0) || (n0 + 32 * NSUB > C + L)) {  // straddles the diagonal or the end
+    if constexpr (MASKED) {
 #pragma unroll
-      for (int u = 0; u < NSUB; ++u) {
+      for (int u = 0; u < 2; ++u) {
         const int room = lim - (n0 + 32 * u + 4 * hf);  // element j is visible iff its offset <= room
 #pragma unroll
         for (int j = 0; j < 16; ++j) st[u][j] = (8 * (j >> 2) + (j & 3) > room) ? -INFINITY : st[u][j];
@@ -349,7 +352,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
     }
     float lmax = st[0][0];
 #pragma unroll
-    for (int u = 0; u < NSUB; ++u)
+    for (int u = 0; u < 2; ++u)
 #pragma unroll
       for (int j = 0; j < 16; ++j) lmax = fmaxf(lmax, st[u][j]);
     const float mt = lmax * c;  // this half's maximum over the tile, log2 units
@@ -364,9 +367,9 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
       mrow = mnew;
     }
 
-    uint32_t pk[NSUB][8];
+    uint32_t pk[2][8];
 #pragma unroll
-    for (int u = 0; u < NSUB; ++u)
+    for (int u = 0; u < 2; ++u)
 #pragma unroll
       for (int jj = 0; jj < 8; ++jj) {
         pk[u][jj] = pack2<E>(fast_exp2(fmaf(st[u][2 * jj], c, -mrow)), fast_exp2(fmaf(st[u][2 * jj + 1], c, -mrow)));
@@ -376,7 +379,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
     // O^T += V^T P^T in k-steps of 16 keys.  In step (u, kk2), element i of lane
     // (ql, hf) stands for key n0 + 32u + 16*kk2 + 8*(i/4) + 4*hf + i%4 on both operands.
 #pragma unroll
-    for (int u = 0; u < NSUB; ++u)
+    for (int u = 0; u < 2; ++u)
 #pragma unroll
       for (int kk2 = 0; kk2 < 2; ++kk2) {
         const uint4 pb = make_uint4(pk[u][4 * kk2], pk[u][4 * kk2 + 1], pk[u][4 * kk2 + 2], pk[u][4 * kk2 + 3]);
@@ -390,20 +393,29 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
         }
       }
   };
-  auto run_tile = [&](int buf, int n0) {
-    if (n0 >= wkend) return;  // every key of the tile is in this wave's future
-    if (n0 + 32 < wkend) tile(std::integral_constant<int, 2>(), buf, n0);
-    else tile(std::integral_constant<int, 1>(), buf, n0);
-  };
 
+  // Tiles below nfull hold keys that every query of the workgroup sees, all
+  // before the prompt end (C + m0 < C + L): no masking.  The remaining tiles
+  // (at most three) straddle a diagonal or the prompt end; a wave skips a
+  // tile that lies wholly in its queries' future.
+  const int ntiles = (kend + BN - 1) / BN;
+  const int nfull = min((C + m0) / BN, ntiles);
   gload(sa, 0);
   lstore(sa, 0);
   __syncthreads();
   int buf = 0;
-  for (int n0 = 0; n0 < kend; n0 += BN, buf ^= 1) {
-    const bool more = n0 + BN < kend;
-    if (more) gload(sa, n0 + BN);
-    run_tile(buf, n0);
+  int tt = 0;
+  for (; tt < nfull; ++tt, buf ^= 1) {
+    const bool more = tt + 1 < ntiles;
+    if (more) gload(sa, (tt + 1) * BN);
+    tile(std::false_type(), buf, tt * BN);
+    if (more) lstore(sa, buf ^ 1);
+    __syncthreads();
+  }
+  for (; tt < ntiles; ++tt, buf ^= 1) {
+    const bool more = tt + 1 < ntiles;
+    if (more) gload(sa, (tt + 1) * BN);
+    if (tt * BN < wkend) tile(std::true_type(), buf, tt * BN);
     if (more) lstore(sa, buf ^ 1);
     __syncthreads();
   }
