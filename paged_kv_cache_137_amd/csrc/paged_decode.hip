@@ -99,16 +99,21 @@ __global__ __launch_bounds__(1024) void decode_plan_kernel(const DecodeArgs a) {
   const int part_tokens = a.part_blocks * BS;
   for (int i = threadIdx.x; i < PLAN_BUCKETS; i += blockDim.x) cnt[i] = 0;
   __syncthreads();
-  for (int s = threadIdx.x; s < a.num_seqs; s += blockDim.x) {
+  // Threads walk the (sequence, partition) pairs directly, so that the loads
+  // of different partitions of one sequence are issued in parallel.
+  const int npairs = a.num_seqs * a.num_parts;
+  for (int i = threadIdx.x; i < npairs; i += blockDim.x) {
+    const int s = i / a.num_parts;
+    const int p = i - s * a.num_parts;
     const int ctx = clamp_ctx(a, s);
     if (ctx <= 0) {
-      atomicAdd(&cnt[0], 1);
+      if (p == 0) atomicAdd(&cnt[0], 1);
       continue;
     }
-    for (int t0 = 0; t0 < ctx; t0 += part_tokens) {
-      const int nb = (min(part_tokens, ctx - t0) + BS - 1) / BS;
-      atomicAdd(&cnt[min(nb, PLAN_BUCKETS - 1)], 1);
-    }
+    const int t0 = p * part_tokens;
+    if (t0 >= ctx) continue;
+    const int nb = (min(part_tokens, ctx - t0) + BS - 1) / BS;
+    atomicAdd(&cnt[min(nb, PLAN_BUCKETS - 1)], 1);
   }
   __syncthreads();
   // Exclusive scan of the bucket counts in descending bucket order: thread i
@@ -138,15 +143,18 @@ __global__ __launch_bounds__(1024) void decode_plan_kernel(const DecodeArgs a) {
     }
   }
   __syncthreads();
-  for (int s = threadIdx.x; s < a.num_seqs; s += blockDim.x) {
+  for (int i = threadIdx.x; i < npairs; i += blockDim.x) {
+    const int s = i / a.num_parts;
+    const int p = i - s * a.num_parts;
     const int ctx = clamp_ctx(a, s);
     if (ctx <= 0) {
-      a.work_list[atomicAdd(&cnt[0], 1)] = (s * a.num_parts) << 1;
+      if (p == 0) a.work_list[atomicAdd(&cnt[0], 1)] = (s * a.num_parts) << 1;
       continue;
     }
+    const int t0 = p * part_tokens;
+    if (t0 >= ctx) continue;
     const int32_t* row = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
-    int p = 0;
-    for (int t0 = 0; t0 < ctx; t0 += part_tokens, ++p) {
+    {
       const int nb = (min(part_tokens, ctx - t0) + BS - 1) / BS;
       // Shared blocks (parallel samples, a common prefix) are read by several
       // sequences close together in time; those partitions are read with
