@@ -124,12 +124,19 @@ template <> struct Store4<f16_t> {
   }
 };
 
-// PAGED = false: keys/values are the prompt's own packed rows (a fresh prompt).
-// PAGED = true:  keys/values are read from the pool through the prompt's block
-//                table.  The first prefix_lens[p] positions are a cached prefix;
-//                the prompt's new tokens follow (their K/V already written).
-template <typename E, typename O, int D, bool PAGED>
+// PB = 0:        keys/values are the prompt's own packed rows (a fresh prompt).
+// PB = 8, 16, 32: keys/values are read from the pool (blocks of PB tokens)
+//                 through the prompt's block table.  The first prefix_lens[p]
+//                 positions are a cached prefix; the prompt's new tokens follow
+//                 (their K/V already written).
+template <typename E, typename O, int D, int PB>
 __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
+  constexpr bool PAGED = PB != 0;
+  constexpr int SH = PB == 8 ? 3 : PB == 16 ? 4 : PB == 32 ? 5 : 0;  // log2 of the block size
+  static_assert(!PAGED || (1 << SH) == PB, "block size 8, 16 or 32");
+  // A wave's 16-byte K chunks of one staging slot cover 512 / D consecutive
+  // rows starting at a multiple of that count, so they sit in one block.
+  static_assert(!PAGED || 512 / D <= PB, "a wave's K rows must share a block");
   // Two quiet NaNs of the element type, packed: the value of a tile whose
   // block id lies outside the pool.
   constexpr uint32_t E16_NAN2 = std::is_same<E, bf16_t>::value ? 0x7fc07fc0u : 0x7e007e00u;
@@ -184,7 +191,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
   int C = 0;
   const int32_t* trow = nullptr;
   if constexpr (PAGED) {
-    const int cap = a.max_blocks_per_seq << a.block_shift;
+    const int cap = a.max_blocks_per_seq << SH;
     C = a.prefix_lens != nullptr ? min(max(a.prefix_lens[pr], 0), cap) : 0;
     L = min(L, cap - C);
     trow = a.block_tables + (int64_t)pr * a.max_blocks_per_seq;
@@ -237,26 +244,49 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
     uint4 v[4];
   };
   Stage sa;
+  // Block ids of the next tile to be staged (paged form only): lane j of each
+  // wave holds the id of the tile's block j.
+  constexpr int NBT = PAGED ? BN / PB : 1;
+  int idv = 0;
+  auto load_ids = [&](int n0) {
+    if constexpr (PAGED) {
+      const int e = (n0 >> SH) + lane;
+      const int last = (C + L - 1) >> SH;  // the table entry of the last key
+      idv = lane < NBT && e <= last ? trow[e] : 0;
+    }
+  };
+  load_ids(0);
   auto gload = [&](Stage& st_, int n0) {
     uint4 (&kst)[KCH] = st_.k;
     uint4 (&vst)[4] = st_.v;
     if constexpr (PAGED) {
-      // Key position -> (physical block from the table, offset in the block).
-      // An id outside the pool yields NaN, so the result shows it.
+      // The tile's NBT block ids were loaded one tile ahead: lane j of every
+      // wave holds block j's id.  Key n0 + r lies in block r >> SH of the
+      // tile, at row r & (PB - 1).  Every load reads inside the pool; an id
+      // outside the pool then yields NaN, so the result shows it, and a key
+      // at or past the end reads as zero.
       const uint4 nanv = make_uint4(E16_NAN2, E16_NAN2, E16_NAN2, E16_NAN2);
-      auto fetch = [&](const void* pool, int key, int ch) -> uint4 {
-        if (key >= C + L) return make_uint4(0u, 0u, 0u, 0u);
-        const int ph = trow[key >> a.block_shift];
-        if ((uint64_t)(uint32_t)ph >= (uint64_t)a.num_blocks) return nanv;
-        const int64_t row = (((int64_t)ph * a.num_heads + h) << a.block_shift) + (key & ((1 << a.block_shift) - 1));
-        return *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(pool) + row * (D * 2) + ch * 16);
+      const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
+      auto fetch = [&](const char* pool, int r, int ph, int ch) -> uint4 {
+        const bool bad = (uint64_t)(uint32_t)ph >= (uint64_t)a.num_blocks;
+        const int64_t row = (((int64_t)(bad ? 0 : ph) * a.num_heads + h) << SH) + (r & (PB - 1));
+        const uint4 x = *reinterpret_cast<const uint4*>(pool + row * (D * 2) + ch * 16);
+        return n0 + r >= C + L ? zero : bad ? nanv : x;
       };
+      const char* kpool = reinterpret_cast<const char*>(a.k_cache);
+      const char* vpool = reinterpret_cast<const char*>(a.v_cache);
 #pragma unroll
-      for (int i = 0; i < KCH; ++i) kst[i] = fetch(a.k_cache, n0 + krow[i], kch[i]);
-      if (threadIdx.x < VG) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) vst[i] = fetch(a.v_cache, n0 + 4 * vg + i, vch);
+      for (int i = 0; i < KCH; ++i) {
+        // The chunk's block is the same for the whole wave.
+        const int j = __builtin_amdgcn_readfirstlane(krow[i] >> SH);
+        kst[i] = fetch(kpool, krow[i], __builtin_amdgcn_readlane(idv, j), kch[i]);
       }
+      if (threadIdx.x < VG) {
+        const int ph = __shfl(idv, (4 * vg) >> SH, 64);  // rows 4vg .. 4vg+3 share a block
+#pragma unroll
+        for (int i = 0; i < 4; ++i) vst[i] = fetch(vpool, 4 * vg + i, ph, vch);
+      }
+      load_ids(n0 + BN);
     } else {
       const char* kt = kb + (int64_t)n0 * rsb;
       const char* vt = vb + (int64_t)n0 * rsb;
@@ -435,26 +465,30 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
   }
 }
 
-template <typename E, typename O, int D, bool PAGED>
+template <typename E, typename O, int D, int PB>
 static hipError_t prefill_t(const PrefillArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL((prefill_kernel<E, O, D, PAGED>), dim3(a.per_xcd * 8), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((prefill_kernel<E, O, D, PB>), dim3(a.per_xcd * 8), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
-template <typename E, bool PAGED>
+template <typename E, int PB>
 static hipError_t prefill_d(const PrefillArgs& a, int out_dtype, int head_dim, hipStream_t st) {
   if (head_dim == 128)
-    return out_dtype == 0 ? prefill_t<E, f32_t, 128, PAGED>(a, st) : prefill_t<E, E, 128, PAGED>(a, st);
-  return out_dtype == 0 ? prefill_t<E, f32_t, 64, PAGED>(a, st) : prefill_t<E, E, 64, PAGED>(a, st);
+    return out_dtype == 0 ? prefill_t<E, f32_t, 128, PB>(a, st) : prefill_t<E, E, 128, PB>(a, st);
+  return out_dtype == 0 ? prefill_t<E, f32_t, 64, PB>(a, st) : prefill_t<E, E, 64, PB>(a, st);
+}
+
+template <typename E>
+static hipError_t prefill_e(const PrefillArgs& a, int out_dtype, int head_dim, hipStream_t st) {
+  if (a.k_cache == nullptr) return prefill_d<E, 0>(a, out_dtype, head_dim, st);
+  if (a.block_shift == 3) return prefill_d<E, 8>(a, out_dtype, head_dim, st);
+  if (a.block_shift == 5) return prefill_d<E, 32>(a, out_dtype, head_dim, st);
+  return prefill_d<E, 16>(a, out_dtype, head_dim, st);
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, int dtype, int out_dtype, int head_dim, hipStream_t st) {
-  if (a.k_cache != nullptr) {
-    if (dtype == 1) return prefill_d<f16_t, true>(a, out_dtype, head_dim, st);
-    return prefill_d<bf16_t, true>(a, out_dtype, head_dim, st);
-  }
-  if (dtype == 1) return prefill_d<f16_t, false>(a, out_dtype, head_dim, st);
-  return prefill_d<bf16_t, false>(a, out_dtype, head_dim, st);
+  if (dtype == 1) return prefill_e<f16_t>(a, out_dtype, head_dim, st);
+  return prefill_e<bf16_t>(a, out_dtype, head_dim, st);
 }
 
 }  // namespace pkv
