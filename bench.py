@@ -22,7 +22,8 @@ The same line also carries:
   mixed_step    the mixed prefill+decode step (8 prompts prefilled while 192
                 sequences decode), per kernel, with prefill's MFMA rate.
   sharing_step  parallel sampling over shared prompt blocks: the batched
-                copy-on-write copy, then decode (logical and unique KV GB/s).
+                copy-on-write copy, then decode (logical and unique KV GB/s),
+                plain and with the shared-prefix decode.
   cached_prefix_prefill  requests prefilling over one cached shared prefix.
   block_size_sweep  the same decode at 8-, 16- and 32-token blocks (the pool's
                 bytes re-tiled, fresh shuffled tables).
@@ -335,8 +336,11 @@ def sharing_step(a, dev, up):
 
     Each group's samples read the prompt's physical blocks; the partly filled
     last prompt block is copied on write (batched pkv_copy_blocks), then every
-    sample decodes.  KV GB/s is reported against both the logical bytes (each
-    sample's whole context) and the unique bytes (distinct slots read).
+    sample decodes, once with the plain decode (every sample reads its whole
+    context through its table) and once with the shared-prefix decode (blocks
+    that a window's samples share are read once for all of them).  KV GB/s is
+    reported against both the logical bytes (each sample's whole context) and
+    the unique bytes (distinct slots read).
     """
     import numpy as np
     import torch
@@ -354,6 +358,11 @@ def sharing_step(a, dev, up):
     dec_ms = _time_events(lambda: ops.paged_attn_decode(t["q"], t["kc"], t["vc"], t["bt"], t["cl"], d.scale, out,
                                                         max_context_len=d.max_context_len, partition_size=512,
                                                         workspace=ws), a.warmup, a.steps)
+    wss = torch.empty(ops.decode_shared_workspace_bytes(S, H, D, d.max_context_len, 512), dtype=torch.uint8,
+                      device=dev)
+    shr_ms = _time_events(lambda: ops.paged_attn_decode_shared(t["q"], t["kc"], t["vc"], t["bt"], t["cl"], d.scale,
+                                                               out, max_context_len=d.max_context_len,
+                                                               partition_size=512, workspace=wss), a.warmup, a.steps)
     used = np.zeros((d.num_blocks, 16), dtype=bool)
     for s_ in range(S):
         n = int(d.context_lens[s_])
@@ -374,6 +383,10 @@ def sharing_step(a, dev, up):
         "decode_ms": round(dec_ms, 4),
         "decode_logical_GBps": round(logical / (dec_ms * 1e-3) / 1e9, 1),
         "decode_unique_GBps": round(unique / (dec_ms * 1e-3) / 1e9, 1),
+        "shared_decode_ms": round(shr_ms, 4),
+        "shared_decode_logical_GBps": round(logical / (shr_ms * 1e-3) / 1e9, 1),
+        "shared_decode_unique_GBps": round(unique / (shr_ms * 1e-3) / 1e9, 1),
+        "shared_decode_unique_frac": round(unique / (shr_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "physical_blocks": d.info["physical_blocks_used"],
         "logical_blocks": d.info["logical_blocks"],
     }

@@ -185,6 +185,35 @@ int pkv_paged_attn_decode_reduce(const void* q, const void* k_cache, const void*
                                  int32_t partition_size, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * pkv_paged_attn_decode_shared - pkv_paged_attn_decode for batches whose
+ * sequences share leading blocks: parallel samples of one request, or
+ * requests with a common prefix, whose tables hold the same physical ids for
+ * those blocks ("vLLM & PagedAttention ...", section VII: blocks shared with
+ * reference counts; "PagedAttention and vLLM, annotated", section 4.4).
+ *
+ * Arguments, preconditions, errors and result are those of
+ * pkv_paged_attn_decode (the same value, up to the order of the fp32 sums),
+ * except that the workspace must hold pkv_decode_shared_workspace_bytes(...).
+ * Sequences are taken in windows of four consecutive ones (0-3, 4-7, ...).
+ * In a window, the sequences whose first block id equals that of the window's
+ * first sequence holding a full block form a group, if there are two or more.
+ * The group's J leading full blocks that all members hold with the same ids
+ * (inside every member's context) are read once, with one online softmax per
+ * member's query.  Each member then attends to its remaining tokens on its
+ * own, and a merge combines the partial results in a fixed order.  Nothing is
+ * assumed about the tables: sharing is found on the device each call, and a
+ * batch without it gives the plain decode's partitions.  Results are
+ * deterministic, bit for bit.
+ */
+size_t pkv_decode_shared_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                                         int32_t max_context_len, int32_t partition_size);
+int pkv_paged_attn_decode_shared(const void* q, const void* k_cache, const void* v_cache, const pkv_cache_desc* desc,
+                                 const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                 int32_t num_seqs, int32_t max_context_len, float scale, void* out,
+                                 int32_t out_dtype, int32_t partition_size, void* workspace, size_t workspace_bytes,
+                                 void* stream);
+
+/*
  * pkv_paged_attn_prefill - causal self-attention over each prompt (prompt phase).
  *
  * All positions of a prompt are known at once, so this is dense matrix-matrix

@@ -15,6 +15,7 @@ from .blocks import BlockManager, OutOfBlocks, slot_mapping  # noqa: F401
 def __getattr__(name):
     # The GPU entry points import torch and load libpkv.so on first use.
     if name in ("kv_cache_write", "paged_attn_decode", "paged_attn_decode_partial", "paged_attn_decode_reduce",
+                "paged_attn_decode_shared", "decode_shared_workspace_bytes",
                 "paged_attn_prefill", "paged_attn_prefill_cached", "decode_workspace_bytes", "copy_blocks",
                 "swap_blocks"):
         from . import ops

@@ -28,6 +28,8 @@ SIGNATURES = {
     "pkv_paged_attn_decode": (_DECODE_ARGS, ctypes.c_int),
     "pkv_paged_attn_decode_partial": (_DECODE_ARGS, ctypes.c_int),
     "pkv_paged_attn_decode_reduce": (_DECODE_ARGS, ctypes.c_int),
+    "pkv_decode_shared_workspace_bytes": ([_i32, _i32, _i32, _i32, _i32], _sz),
+    "pkv_paged_attn_decode_shared": (_DECODE_ARGS, ctypes.c_int),
     "pkv_copy_blocks": ([_vp, _vp, _vp, _vp, _i64, _vp], ctypes.c_int),
     "pkv_swap_blocks": ([_vp, _vp, _i64, _vp, _vp, _i64, _vp, _vp, _i64, _vp], ctypes.c_int),
     "pkv_paged_attn_prefill_cached": (

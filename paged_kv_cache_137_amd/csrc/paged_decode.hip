@@ -89,6 +89,9 @@ struct DecodeGeom {
 };
 
 __device__ __forceinline__ int clamp_ctx(const DecodeArgs& a, int s) { return min(a.context_lens[s], a.max_context_len); }
+// First token of a sequence's own partitions: past the blocks its sharing
+// group reads for it (shared-prefix form), else 0.
+__device__ __forceinline__ int seq_start(const DecodeArgs& a, int s) { return a.tok_start ? a.tok_start[s] : 0; }
 
 // List every (sequence, partition) that holds tokens, largest partitions first,
 // and reset the work counter.  A sequence with context_len <= 0 gets one entry
@@ -110,7 +113,7 @@ __global__ __launch_bounds__(1024) void decode_plan_kernel(const DecodeArgs a) {
       if (p == 0) atomicAdd(&cnt[0], 1);
       continue;
     }
-    const int t0 = p * part_tokens;
+    const int t0 = seq_start(a, s) + p * part_tokens;
     if (t0 >= ctx) continue;
     const int nb = (min(part_tokens, ctx - t0) + BS - 1) / BS;
     atomicAdd(&cnt[min(nb, PLAN_BUCKETS - 1)], 1);
@@ -140,6 +143,7 @@ __global__ __launch_bounds__(1024) void decode_plan_kernel(const DecodeArgs a) {
     if (i == PLAN_BUCKETS - 1) {
       a.work_ctrl[0] = 0;
       a.work_ctrl[1] = before + incl;
+      a.work_ctrl[2] = 0;
     }
   }
   __syncthreads();
@@ -151,7 +155,7 @@ __global__ __launch_bounds__(1024) void decode_plan_kernel(const DecodeArgs a) {
       if (p == 0) a.work_list[atomicAdd(&cnt[0], 1)] = (s * a.num_parts) << 1;
       continue;
     }
-    const int t0 = p * part_tokens;
+    const int t0 = seq_start(a, s) + p * part_tokens;
     if (t0 >= ctx) continue;
     const int32_t* row = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
     {
@@ -161,7 +165,7 @@ __global__ __launch_bounds__(1024) void decode_plan_kernel(const DecodeArgs a) {
       // cached loads so that the repeats hit in L2.  The sign of sharing used:
       // a neighbouring sequence holds the same physical block at the
       // partition's first logical position.
-      const int lb = p * a.part_blocks;
+      const int lb = t0 / BS;
       const int mine = row[lb];
       int shared = 0;
       for (int s2 = max(s - 1, 0); s2 <= min(s + 1, a.num_seqs - 1); ++s2)
@@ -206,13 +210,15 @@ __global__ __launch_bounds__(NW * 64) void decode_partial_kernel(const DecodeArg
     const int p = entry - s * a.num_parts;
     const int64_t sh = (int64_t)s * H + h;
     const int ctx = clamp_ctx(a, s);
-    const int tok0 = p * part_tokens;
+    const int st0 = seq_start(a, s);
+    const int tok0 = st0 + p * part_tokens;
     if (ctx <= 0) {  // undefined attention: report NaN rather than garbage
       for (int t = lane; t < D; t += 64) Out<O>::put(a.out, sh * D + t, __builtin_nanf(""));
       continue;
     }
     if (tok0 >= ctx) continue;
-    const int nparts = (ctx + part_tokens - 1) / part_tokens;
+    const int nparts = (ctx - st0 + part_tokens - 1) / part_tokens;
+    const bool direct = nparts == 1 && st0 == 0;  // the whole context is this unit's
     const int nblk = (min(part_tokens, ctx - tok0) + BS - 1) / BS;
 
     const uint4 qv = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(a.q) + sh * (D * G::ES) + c * 16);
@@ -331,7 +337,7 @@ __global__ __launch_bounds__(NW * 64) void decode_partial_kernel(const DecodeArg
       for (int e2 = 0; e2 < VEC; ++e2) acc[e2] += __shfl_xor(acc[e2], sft, 64);
     }
     if (r == 0) {
-      if (nparts == 1) {
+      if (direct) {
 #pragma unroll
         for (int e2 = 0; e2 < VEC; ++e2) Out<O>::put(a.out, sh * D + c * VEC + e2, acc[e2] / Ls);
       } else {
@@ -372,10 +378,287 @@ __global__ __launch_bounds__(D) void decode_reduce_kernel(const DecodeArgs a) {
   Out<O>::put(a.out, sh * D + t, A / Ls);
 }
 
-// Workgroups of the persistent kernel: enough to fill every CU of the device
-// at the kernel's occupancy, never more than there are units.
-template <typename K>
-static int persistent_grid(K kernel, int block, int64_t units) {
+// ---------------------------------------------------------------------------
+// Shared-prefix decode.  Parallel samples of one request, or requests with a
+// common prefix, hold the same physical blocks at the start of their tables
+// ("vLLM & PagedAttention ...", section VII: shared blocks with reference
+// counts).  Reading such a block once for all the sequences that hold it, with
+// one query per sequence, gives the same attention with fewer bytes.
+//
+// Sequences are taken in windows of SHARE_WINDOW consecutive ones.  The
+// leader of a window is its first sequence that holds a full block; the
+// members are the window's sequences whose first block id is the leader's.
+// J is the number of leading full blocks that every member holds with the
+// leader's ids, all inside every member's context.  A window with two or more
+// members and J >= 1 is a group: decode_group_kernel reads its J blocks once,
+// in partitions, and writes one partial result per member; each member then
+// attends to tokens J*BS .. ctx-1 on its own (decode_partial_kernel, with
+// tok_start), and the reduce merges both kinds of partial results.
+
+// One wave per window.
+__global__ __launch_bounds__(1024) void share_detect_kernel(const DecodeArgs a) {
+  constexpr int GW = SHARE_WINDOW;
+  const int lane = threadIdx.x & 63;
+  const int win = blockIdx.x * 16 + (threadIdx.x >> 6);
+  if (win >= a.num_windows) return;
+  const int BS = a.block_size;
+  const int s0 = win * GW;
+  int nfull[GW];
+  const int32_t* rows[GW];
+#pragma unroll
+  for (int i = 0; i < GW; ++i) {
+    const int s = s0 + i;
+    nfull[i] = s < a.num_seqs ? max(clamp_ctx(a, s), 0) / BS : 0;
+    rows[i] = a.block_tables + (int64_t)min(s, a.num_seqs - 1) * a.max_blocks_per_seq;
+  }
+  int lead = -1;
+#pragma unroll
+  for (int i = GW - 1; i >= 0; --i)
+    if (nfull[i] >= 1) lead = i;
+  int mask = 0, J = 0;
+  if (lead >= 0) {
+    const int32_t* lrow = a.block_tables + (int64_t)(s0 + lead) * a.max_blocks_per_seq;
+    const int first = lrow[0];
+    int lim = nfull[lead];
+    mask = 1 << lead;
+#pragma unroll
+    for (int i = 0; i < GW; ++i)
+      if (i != lead && nfull[i] >= 1 && rows[i][0] == first) {
+        mask |= 1 << i;
+        lim = min(lim, nfull[i]);
+      }
+    if (__builtin_popcount(mask) >= 2) {
+      // The first block where some member's id differs from the leader's.
+      J = lim;
+      for (int j0 = 0; j0 < lim; j0 += 64) {
+        const int j = j0 + lane;
+        bool diff = false;
+        if (j < lim) {
+          const int lv = lrow[j];
+#pragma unroll
+          for (int i = 0; i < GW; ++i)
+            if ((mask >> i) & 1) diff |= rows[i][j] != lv;
+        }
+        const unsigned long long b = __ballot(diff);
+        if (b != 0ull) {
+          J = j0 + __builtin_ctzll(b);
+          break;
+        }
+      }
+    }
+  }
+  const bool grp = __builtin_popcount(mask) >= 2 && J >= 1;
+  if (lane == 0) a.win_info[win] = grp ? (J << 4) | mask : 0;
+  if (lane < GW && s0 + lane < a.num_seqs) a.tok_start[s0 + lane] = grp && ((mask >> lane) & 1) ? J * BS : 0;
+}
+
+// Persistent kernel over (window, partition of the shared blocks, NW heads)
+// units.  Wave w streams head NW*g + w of the group's shared blocks once and
+// keeps one online softmax per member (its own query), with the same lane
+// layout as decode_partial_kernel.  Every shared block is full and inside
+// every member's context, so no slot is masked.
+template <typename E, typename O, int D, int BS>
+__global__ __launch_bounds__(NW * 64) void decode_group_kernel(const DecodeArgs a) {
+  using G = DecodeGeom<E, D, BS>;
+  using C = Chunk<E>;
+  constexpr int VEC = G::VEC, LPT = G::LPT, NI = G::NI;
+  constexpr int GW = SHARE_WINDOW;
+
+  __shared__ int sm_unit[2];
+
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r = lane / LPT;
+  const int c = lane % LPT;
+  const int H = a.num_heads;
+  const int HG = (H + NW - 1) / NW;
+  const int part_tokens = a.part_blocks * BS;
+  const int total = a.num_windows * a.num_parts * HG;
+  const int64_t bstride = (int64_t)H * G::TILE;
+
+  for (int it = 0;; ++it) {
+    if (threadIdx.x == 0) sm_unit[it & 1] = atomicAdd(&a.work_ctrl[2], 1);
+    __syncthreads();
+    const int u = __builtin_amdgcn_readfirstlane(sm_unit[it & 1]);
+    if (u >= total) break;
+    const int e = u / HG;
+    const int h = (u - e * HG) * NW + w;
+    if (h >= H) continue;
+    const int win = e / a.num_parts;
+    const int p = e - win * a.num_parts;
+    const int info = __builtin_amdgcn_readfirstlane(a.win_info[win]);
+    if (info == 0) continue;
+    const int J = info >> 4, mask = info & 15;
+    const int tok0 = p * part_tokens;
+    const int tend = min(tok0 + part_tokens, J * BS);
+    if (tok0 >= tend) continue;
+    const int nblk = (tend - tok0) / BS;
+    const int s0 = win * GW;
+
+    uint4 qv[GW];
+    float m[GW], l[GW], acc[GW][VEC];
+#pragma unroll
+    for (int i = 0; i < GW; ++i) {
+      qv[i] = make_uint4(0u, 0u, 0u, 0u);
+      if ((mask >> i) & 1)
+        qv[i] = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(a.q) +
+                                                ((int64_t)(s0 + i) * H + h) * (D * G::ES) + c * 16);
+      m[i] = NEG_BIG;
+      l[i] = 0.f;
+#pragma unroll
+      for (int e2 = 0; e2 < VEC; ++e2) acc[i][e2] = 0.f;
+    }
+    const char* kbase = reinterpret_cast<const char*>(a.k_cache) + (int64_t)h * G::TILE + lane * 16;
+    const char* vbase = reinterpret_cast<const char*>(a.v_cache) + (int64_t)h * G::TILE + lane * 16;
+    const int lead = __builtin_ctz(mask);
+    const int32_t* trow = a.block_tables + (int64_t)(s0 + lead) * a.max_blocks_per_seq + tok0 / BS;
+
+    auto consume = [&](const uint4 (&kx)[NI], const uint4 (&vx)[NI], bool bad) {
+      float vf[NI][VEC];
+#pragma unroll
+      for (int i = 0; i < NI; ++i) C::unpack(vx[i], vf[i]);
+#pragma unroll
+      for (int g = 0; g < GW; ++g) {
+        if (!((mask >> g) & 1)) continue;
+        float sc[NI];
+#pragma unroll
+        for (int i = 0; i < NI; ++i) sc[i] = group_sum<LPT>(C::dot(qv[g], kx[i])) * a.scale_log2;
+        if (bad) {
+#pragma unroll
+          for (int i = 0; i < NI; ++i) sc[i] = __builtin_nanf("");
+        }
+        float mx = m[g];
+#pragma unroll
+        for (int i = 0; i < NI; ++i) mx = fmaxf(mx, sc[i]);
+        const float alpha = fast_exp2(m[g] - mx);
+        m[g] = mx;
+        l[g] *= alpha;
+#pragma unroll
+        for (int e2 = 0; e2 < VEC; ++e2) acc[g][e2] *= alpha;
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+          const float pi = fast_exp2(sc[i] - mx);
+          l[g] += pi;
+#pragma unroll
+          for (int e2 = 0; e2 < VEC; ++e2) acc[g][e2] = fmaf(pi, vf[i][e2], acc[g][e2]);
+        }
+      }
+    };
+    auto load = [&](int phys, uint4 (&kx)[NI], uint4 (&vx)[NI]) {
+      const char* kp = kbase + (int64_t)phys * bstride;
+      const char* vp = vbase + (int64_t)phys * bstride;
+#pragma unroll
+      for (int i = 0; i < NI; ++i) kx[i] = load_kv16<true>(kp + i * 1024);
+#pragma unroll
+      for (int i = 0; i < NI; ++i) vx[i] = load_kv16<true>(vp + i * 1024);
+    };
+    for (int cb = 0; cb < nblk; cb += 64) {
+      const int cn = min(64, nblk - cb);
+      const int tv = lane < cn ? trow[cb + lane] : 0;
+      auto phys_of = [&](int j, bool& bad) {
+        const int ph = __builtin_amdgcn_readlane(tv, j);
+        bad = (uint64_t)(uint32_t)ph >= (uint64_t)a.num_blocks;
+        return bad ? 0 : ph;
+      };
+      int j = 0;
+      if constexpr (G::PINGPONG) {
+        uint4 kA[NI], vA[NI], kB[NI], vB[NI];
+        bool badA, badB;
+        load(phys_of(j, badA), kA, vA);
+        while (j + 2 < cn) {
+          load(phys_of(j + 1, badB), kB, vB);
+          consume(kA, vA, badA);
+          load(phys_of(j + 2, badA), kA, vA);
+          consume(kB, vB, badB);
+          j += 2;
+        }
+        if (j + 1 < cn) {
+          load(phys_of(j + 1, badB), kB, vB);
+          consume(kA, vA, badA);
+          consume(kB, vB, badB);
+        } else {
+          consume(kA, vA, badA);
+        }
+      } else {
+        for (; j < cn; ++j) {
+          uint4 kA[NI], vA[NI];
+          bool badA;
+          load(phys_of(j, badA), kA, vA);
+          consume(kA, vA, badA);
+        }
+      }
+    }
+
+    // Per member: merge the wave's token rows, then store the partial result.
+#pragma unroll
+    for (int g = 0; g < GW; ++g) {
+      if (!((mask >> g) & 1)) continue;
+      float M = m[g];
+#pragma unroll
+      for (int sft = LPT; sft < 64; sft <<= 1) M = fmaxf(M, __shfl_xor(M, sft, 64));
+      const float f = fast_exp2(m[g] - M);
+      float Ls = l[g] * f;
+      float av[VEC];
+#pragma unroll
+      for (int e2 = 0; e2 < VEC; ++e2) av[e2] = acc[g][e2] * f;
+#pragma unroll
+      for (int sft = LPT; sft < 64; sft <<= 1) {
+        Ls += __shfl_xor(Ls, sft, 64);
+#pragma unroll
+        for (int e2 = 0; e2 < VEC; ++e2) av[e2] += __shfl_xor(av[e2], sft, 64);
+      }
+      if (r == 0) {
+        const int64_t pi = ((int64_t)(s0 + g) * H + h) * a.num_parts + p;
+        float* dst = a.ws_acc_sh + pi * D + c * VEC;
+#pragma unroll
+        for (int e2 = 0; e2 < VEC; e2 += 4)
+          *reinterpret_cast<float4*>(dst + e2) = make_float4(av[e2], av[e2 + 1], av[e2 + 2], av[e2 + 3]);
+        if (c == 0) *reinterpret_cast<float2*>(a.ws_ml_sh + pi * 2) = make_float2(M, Ls);
+      }
+    }
+  }
+}
+
+// Merge of the shared-prefix form: the group's partial results over the
+// shared blocks (partitions ascending), then the sequence's own (ascending).
+// A sequence outside any group with one partition was finished by the
+// partial kernel.
+template <typename O, int D>
+__global__ __launch_bounds__(D) void decode_reduce_shared_kernel(const DecodeArgs a) {
+  const int s = blockIdx.x;
+  const int h = blockIdx.y;
+  const int ctx = clamp_ctx(a, s);
+  if (ctx <= 0) return;
+  const int part_tokens = a.part_blocks * a.block_size;
+  const int st0 = a.tok_start[s];
+  const int nsh = (st0 + part_tokens - 1) / part_tokens;
+  const int npriv = (ctx - st0 + part_tokens - 1) / part_tokens;
+  if (st0 == 0 && npriv <= 1) return;
+  const int t = threadIdx.x;
+  const int64_t sh = (int64_t)s * a.num_heads + h;
+  const int64_t base = sh * a.num_parts;
+  float M = NEG_BIG;
+  for (int p = 0; p < nsh; ++p) M = fmaxf(M, a.ws_ml_sh[(base + p) * 2]);
+  for (int p = 0; p < npriv; ++p) M = fmaxf(M, a.ws_ml[(base + p) * 2]);
+  float Ls = 0.f, A = 0.f;
+  for (int p = 0; p < nsh; ++p) {
+    const float f = fast_exp2(a.ws_ml_sh[(base + p) * 2] - M);
+    Ls = fmaf(a.ws_ml_sh[(base + p) * 2 + 1], f, Ls);
+    A = fmaf(a.ws_acc_sh[(base + p) * D + t], f, A);
+  }
+  for (int p = 0; p < npriv; ++p) {
+    const float f = fast_exp2(a.ws_ml[(base + p) * 2] - M);
+    Ls = fmaf(a.ws_ml[(base + p) * 2 + 1], f, Ls);
+    A = fmaf(a.ws_acc[(base + p) * D + t], f, A);
+  }
+  Out<O>::put(a.out, sh * D + t, A / Ls);
+}
+
+// Workgroups of a persistent kernel: enough to fill every CU of the device
+// at the kernel's occupancy, never more than there are units.  Cached per
+// kernel and device.
+template <auto KERNEL>
+static int persistent_grid(int block, int64_t units) {
   constexpr int kMaxDev = 64;
   static int slots[kMaxDev];
   int dev = 0;
@@ -384,7 +667,7 @@ static int persistent_grid(K kernel, int block, int64_t units) {
   if (n == 0) {
     int cus = 0, occ = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, block, 0) != hipSuccess || occ <= 0) occ = 1;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, KERNEL, block, 0) != hipSuccess || occ <= 0) occ = 1;
     n = cus * occ;
     if (dev < kMaxDev) slots[dev] = n;
   }
@@ -394,7 +677,7 @@ static int persistent_grid(K kernel, int block, int64_t units) {
 template <typename E, typename O, int D, int BS>
 static hipError_t partial_bs(const DecodeArgs& a, hipStream_t st) {
   hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(1024), 0, st, a);
-  const int grid = persistent_grid(decode_partial_kernel<E, O, D, BS>, NW * 64, ((int64_t)a.total_units + NW - 1) / NW);
+  const int grid = persistent_grid<decode_partial_kernel<E, O, D, BS>>(NW * 64, ((int64_t)a.total_units + NW - 1) / NW);
   hipLaunchKernelGGL((decode_partial_kernel<E, O, D, BS>), dim3(grid), dim3(NW * 64), 0, st, a);
   return hipGetLastError();
 }
@@ -439,6 +722,59 @@ hipError_t launch_decode_reduce(const DecodeArgs& a, int out_dtype, int head_dim
   if (out_dtype == 0) return reduce_t<f32_t, 64>(a, st);
   if (out_dtype == 1) return reduce_t<f16_t, 64>(a, st);
   return reduce_t<bf16_t, 64>(a, st);
+}
+
+template <typename E, typename O, int D, int BS>
+static hipError_t shared_bs(const DecodeArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL(share_detect_kernel, dim3((a.num_windows + 15) / 16), dim3(1024), 0, st, a);
+  hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(1024), 0, st, a);
+  const int64_t gunits = (int64_t)a.num_windows * a.num_parts * ((a.num_heads + NW - 1) / NW);
+  const int ggrid = persistent_grid<decode_group_kernel<E, O, D, BS>>(NW * 64, gunits);
+  hipLaunchKernelGGL((decode_group_kernel<E, O, D, BS>), dim3(ggrid), dim3(NW * 64), 0, st, a);
+  const int grid = persistent_grid<decode_partial_kernel<E, O, D, BS>>(NW * 64, ((int64_t)a.total_units + NW - 1) / NW);
+  hipLaunchKernelGGL((decode_partial_kernel<E, O, D, BS>), dim3(grid), dim3(NW * 64), 0, st, a);
+  return hipGetLastError();
+}
+
+template <typename E, typename O, int D>
+static hipError_t shared_t(const DecodeArgs& a, hipStream_t st) {
+  if (a.block_size == 8) return shared_bs<E, O, D, 8>(a, st);
+  if (a.block_size == 32) return shared_bs<E, O, D, 32>(a, st);
+  return shared_bs<E, O, D, 16>(a, st);
+}
+
+template <typename E, int D>
+static hipError_t shared_out(const DecodeArgs& a, int out_dtype, hipStream_t st) {
+  if (out_dtype == 0) return shared_t<E, f32_t, D>(a, st);
+  return shared_t<E, E, D>(a, st);
+}
+
+hipError_t launch_decode_shared_partial(const DecodeArgs& a, int dtype, int out_dtype, int head_dim, hipStream_t st) {
+  if (head_dim == 128) {
+    if (dtype == 0) return shared_t<f32_t, f32_t, 128>(a, st);
+    if (dtype == 1) return shared_out<f16_t, 128>(a, out_dtype, st);
+    return shared_out<bf16_t, 128>(a, out_dtype, st);
+  }
+  if (dtype == 0) return shared_t<f32_t, f32_t, 64>(a, st);
+  if (dtype == 1) return shared_out<f16_t, 64>(a, out_dtype, st);
+  return shared_out<bf16_t, 64>(a, out_dtype, st);
+}
+
+template <typename O, int D>
+static hipError_t reduce_shared_t(const DecodeArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL((decode_reduce_shared_kernel<O, D>), dim3(a.num_seqs, a.num_heads), dim3(D), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_shared_reduce(const DecodeArgs& a, int out_dtype, int head_dim, hipStream_t st) {
+  if (head_dim == 128) {
+    if (out_dtype == 0) return reduce_shared_t<f32_t, 128>(a, st);
+    if (out_dtype == 1) return reduce_shared_t<f16_t, 128>(a, st);
+    return reduce_shared_t<bf16_t, 128>(a, st);
+  }
+  if (out_dtype == 0) return reduce_shared_t<f32_t, 64>(a, st);
+  if (out_dtype == 1) return reduce_shared_t<f16_t, 64>(a, st);
+  return reduce_shared_t<bf16_t, 64>(a, st);
 }
 
 }  // namespace pkv

@@ -67,17 +67,25 @@ bool copy_to_host(std::vector<T>& dst, const T* src, size_t n, hipStream_t st) {
 //   work_list  S * P int32
 //   ws_acc     S * H * P * D float   (only when P > 1)
 //   ws_ml      S * H * P * 2 float   (only when P > 1)
+// The shared-prefix form always has the partial regions (a sequence with one
+// partition of its own still merges it with its group's), followed by
+//   tok_start  S int32
+//   win_info   W int32, W = ceil(S / SHARE_WINDOW)
+//   acc_sh     S * H * P * D float
+//   ml_sh      S * H * P * 2 float
 struct DecodePlan {
   int32_t part_blocks = 0;
   int32_t num_parts = 0;
+  int32_t num_windows = 0;
   size_t list_off = 0, acc_off = 0, ml_off = 0;
+  size_t start_off = 0, win_off = 0, acc_sh_off = 0, ml_sh_off = 0;
   size_t ws_bytes = 0;
 };
 
 size_t align16(size_t x) { return (x + 15) & ~(size_t)15; }
 
 DecodePlan plan_decode(int32_t num_seqs, int32_t num_heads, int32_t head_dim, int32_t max_context_len,
-                       int32_t partition_size, int32_t block_size = kBlock) {
+                       int32_t partition_size, int32_t block_size = kBlock, bool shared = false) {
   DecodePlan p;
   if (partition_size == 0) {
     p.part_blocks = (max_context_len + block_size - 1) / block_size;
@@ -87,16 +95,26 @@ DecodePlan plan_decode(int32_t num_seqs, int32_t num_heads, int32_t head_dim, in
     p.num_parts = (max_context_len + partition_size - 1) / partition_size;
   }
   const size_t units = (size_t)num_seqs * num_heads * p.num_parts;
+  const bool partials = shared || p.num_parts > 1;
   p.list_off = 16;
   p.acc_off = p.list_off + align16((size_t)num_seqs * p.num_parts * sizeof(int32_t));
-  p.ml_off = p.acc_off + (p.num_parts > 1 ? units * head_dim * sizeof(float) : 0);
-  p.ws_bytes = p.ml_off + (p.num_parts > 1 ? units * 2 * sizeof(float) : 0);
+  p.ml_off = p.acc_off + (partials ? units * head_dim * sizeof(float) : 0);
+  p.ws_bytes = p.ml_off + (partials ? units * 2 * sizeof(float) : 0);
+  if (shared) {
+    p.num_windows = (num_seqs + pkv::SHARE_WINDOW - 1) / pkv::SHARE_WINDOW;
+    p.start_off = align16(p.ws_bytes);
+    p.win_off = p.start_off + align16((size_t)num_seqs * sizeof(int32_t));
+    p.acc_sh_off = p.win_off + align16((size_t)p.num_windows * sizeof(int32_t));
+    p.ml_sh_off = p.acc_sh_off + units * head_dim * sizeof(float);
+    p.ws_bytes = p.ml_sh_off + units * 2 * sizeof(float);
+  }
   return p;
 }
 
 enum Stage { kPartial = 1, kReduce = 2, kBoth = 3 };
 
-int decode_impl(int stages, const void* q, const void* k_cache, const void* v_cache, const pkv_cache_desc* desc,
+int decode_impl(int stages, bool shared, const void* q, const void* k_cache, const void* v_cache,
+                const pkv_cache_desc* desc,
                 const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
                 int32_t num_seqs, int32_t max_context_len, float scale, void* out, int32_t out_dtype,
                 int32_t partition_size, void* workspace, size_t workspace_bytes, void* stream) {
@@ -113,7 +131,7 @@ int decode_impl(int stages, const void* q, const void* k_cache, const void* v_ca
   if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16)) return PKV_EINVAL;
   if (!aligned(block_tables, 4) || !aligned(context_lens, 4)) return PKV_EINVAL;
   const DecodePlan plan =
-      plan_decode(num_seqs, desc->num_heads, desc->head_dim, max_context_len, partition_size, bsz);
+      plan_decode(num_seqs, desc->num_heads, desc->head_dim, max_context_len, partition_size, bsz, shared);
   const int64_t units = (int64_t)num_seqs * desc->num_heads * plan.num_parts;
   if (units > ((int64_t)1 << 31) - 64 || num_seqs > 65535 * 32768) return PKV_EINVAL;
   if ((int64_t)num_seqs * plan.num_parts >= ((int64_t)1 << 30)) return PKV_EINVAL;  // work-list entries carry a tag bit
@@ -148,8 +166,16 @@ int decode_impl(int stages, const void* q, const void* k_cache, const void* v_ca
   char* ws = reinterpret_cast<char*>(workspace);
   a.work_ctrl = reinterpret_cast<int32_t*>(ws);
   a.work_list = reinterpret_cast<int32_t*>(ws + plan.list_off);
-  a.ws_acc = plan.num_parts > 1 ? reinterpret_cast<float*>(ws + plan.acc_off) : nullptr;
-  a.ws_ml = plan.num_parts > 1 ? reinterpret_cast<float*>(ws + plan.ml_off) : nullptr;
+  const bool partials = shared || plan.num_parts > 1;
+  a.ws_acc = partials ? reinterpret_cast<float*>(ws + plan.acc_off) : nullptr;
+  a.ws_ml = partials ? reinterpret_cast<float*>(ws + plan.ml_off) : nullptr;
+  if (shared) {
+    a.tok_start = reinterpret_cast<int32_t*>(ws + plan.start_off);
+    a.win_info = reinterpret_cast<int32_t*>(ws + plan.win_off);
+    a.ws_acc_sh = reinterpret_cast<float*>(ws + plan.acc_sh_off);
+    a.ws_ml_sh = reinterpret_cast<float*>(ws + plan.ml_sh_off);
+    a.num_windows = plan.num_windows;
+  }
   a.num_blocks = desc->num_blocks;
   a.num_heads = desc->num_heads;
   a.max_blocks_per_seq = max_blocks_per_seq;
@@ -161,6 +187,11 @@ int decode_impl(int stages, const void* q, const void* k_cache, const void* v_ca
   a.total_units = (int32_t)units;
   a.scale_log2 = scale * 1.4426950408889634f;
 
+  if (shared) {
+    st = launch_status(pkv::launch_decode_shared_partial(a, desc->dtype, out_dtype, desc->head_dim, sm));
+    if (st != PKV_OK) return st;
+    return launch_status(pkv::launch_decode_shared_reduce(a, out_dtype, desc->head_dim, sm));
+  }
   if (stages & kPartial) {
     st = launch_status(pkv::launch_decode_partial(a, desc->dtype, out_dtype, desc->head_dim, sm));
     if (st != PKV_OK) return st;
@@ -238,11 +269,27 @@ size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t h
   return plan_decode(num_seqs, num_heads, head_dim, max_context_len, partition_size).ws_bytes;
 }
 
+size_t pkv_decode_shared_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                                         int32_t max_context_len, int32_t partition_size) {
+  if (num_seqs <= 0 || num_heads <= 0 || head_dim <= 0 || max_context_len <= 0 || partition_size < 0) return 0;
+  return plan_decode(num_seqs, num_heads, head_dim, max_context_len, partition_size, kBlock, true).ws_bytes;
+}
+
+int pkv_paged_attn_decode_shared(const void* q, const void* k_cache, const void* v_cache, const pkv_cache_desc* desc,
+                                 const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                 int32_t num_seqs, int32_t max_context_len, float scale, void* out,
+                                 int32_t out_dtype, int32_t partition_size, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+  return decode_impl(kBoth, true, q, k_cache, v_cache, desc, block_tables, max_blocks_per_seq, context_lens,
+                     num_seqs, max_context_len, scale, out, out_dtype, partition_size, workspace, workspace_bytes,
+                     stream);
+}
+
 int pkv_paged_attn_decode(const void* q, const void* k_cache, const void* v_cache, const pkv_cache_desc* desc,
                           const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
                           int32_t num_seqs, int32_t max_context_len, float scale, void* out, int32_t out_dtype,
                           int32_t partition_size, void* workspace, size_t workspace_bytes, void* stream) {
-  return decode_impl(kBoth, q, k_cache, v_cache, desc, block_tables, max_blocks_per_seq, context_lens, num_seqs,
+  return decode_impl(kBoth, false, q, k_cache, v_cache, desc, block_tables, max_blocks_per_seq, context_lens, num_seqs,
                      max_context_len, scale, out, out_dtype, partition_size, workspace, workspace_bytes, stream);
 }
 
@@ -251,7 +298,7 @@ int pkv_paged_attn_decode_partial(const void* q, const void* k_cache, const void
                                   int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
                                   int32_t max_context_len, float scale, void* out, int32_t out_dtype,
                                   int32_t partition_size, void* workspace, size_t workspace_bytes, void* stream) {
-  return decode_impl(kPartial, q, k_cache, v_cache, desc, block_tables, max_blocks_per_seq, context_lens, num_seqs,
+  return decode_impl(kPartial, false, q, k_cache, v_cache, desc, block_tables, max_blocks_per_seq, context_lens, num_seqs,
                      max_context_len, scale, out, out_dtype, partition_size, workspace, workspace_bytes, stream);
 }
 
@@ -260,7 +307,7 @@ int pkv_paged_attn_decode_reduce(const void* q, const void* k_cache, const void*
                                  int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
                                  int32_t max_context_len, float scale, void* out, int32_t out_dtype,
                                  int32_t partition_size, void* workspace, size_t workspace_bytes, void* stream) {
-  return decode_impl(kReduce, q, k_cache, v_cache, desc, block_tables, max_blocks_per_seq, context_lens, num_seqs,
+  return decode_impl(kReduce, false, q, k_cache, v_cache, desc, block_tables, max_blocks_per_seq, context_lens, num_seqs,
                      max_context_len, scale, out, out_dtype, partition_size, workspace, workspace_bytes, stream);
 }
 

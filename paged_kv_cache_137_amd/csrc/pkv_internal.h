@@ -32,7 +32,16 @@ struct DecodeArgs {
   float* ws_acc;      // [S][H][P][D] unnormalised partial outputs
   float* ws_ml;       // [S][H][P][2]  running max (log2 units) and sum
   int32_t* work_list; // [S*P] (sequence, partition) entries, largest partitions first
-  int32_t* work_ctrl; // [0] next unit to claim, [1] number of entries in work_list
+  int32_t* work_ctrl; // [0] next unit to claim, [1] number of entries in work_list,
+                      // [2] next shared-prefix unit to claim
+  // Shared-prefix form only (null otherwise): sequences are taken in windows
+  // of SHARE_WINDOW consecutive ones; the members of a window that hold the
+  // same leading blocks form a group whose shared blocks are read once.
+  int32_t* tok_start; // [S] first token a sequence attends to on its own (0: no group)
+  int32_t* win_info;  // [W] (shared full blocks J << 4) | member mask, or 0
+  float* ws_acc_sh;   // [S][H][P][D] partial outputs over the shared blocks
+  float* ws_ml_sh;    // [S][H][P][2]
+  int32_t num_windows;
   int64_t num_blocks;
   int32_t num_heads;
   int32_t max_blocks_per_seq;
@@ -90,6 +99,14 @@ hipError_t launch_copy_blocks(const CopyArgs& a, hipStream_t stream);
 hipError_t launch_kv_cache_write(const WriteArgs& a, hipStream_t stream);
 hipError_t launch_decode_partial(const DecodeArgs& a, int dtype, int out_dtype, int head_dim, hipStream_t stream);
 hipError_t launch_decode_reduce(const DecodeArgs& a, int out_dtype, int head_dim, hipStream_t stream);
+// Shared-prefix decode: detection, plan, group and per-sequence kernels; then the merge.
+hipError_t launch_decode_shared_partial(const DecodeArgs& a, int dtype, int out_dtype, int head_dim,
+                                        hipStream_t stream);
+hipError_t launch_decode_shared_reduce(const DecodeArgs& a, int out_dtype, int head_dim, hipStream_t stream);
+
+// Sequences per sharing window of the shared-prefix decode (a group has at
+// most this many members).
+constexpr int SHARE_WINDOW = 4;
 hipError_t launch_prefill(const PrefillArgs& a, int dtype, int out_dtype, int head_dim, hipStream_t stream);
 
 // Prefill query-tile height (rows per workgroup).

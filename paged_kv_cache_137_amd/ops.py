@@ -96,6 +96,12 @@ def decode_workspace_bytes(num_seqs: int, num_heads: int, head_dim: int, max_con
     return int(lib().pkv_decode_workspace_bytes(num_seqs, num_heads, head_dim, max_context_len, partition_size))
 
 
+def decode_shared_workspace_bytes(num_seqs: int, num_heads: int, head_dim: int, max_context_len: int,
+                                  partition_size: int = DEFAULT_PARTITION) -> int:
+    return int(lib().pkv_decode_shared_workspace_bytes(num_seqs, num_heads, head_dim, max_context_len,
+                                                       partition_size))
+
+
 def _decode_call(fn_name, q, k_cache, v_cache, block_tables, context_lens, scale, out,
                  max_context_len, partition_size, workspace):
     _need(k_cache, "k_cache", dim=4)
@@ -117,7 +123,8 @@ def _decode_call(fn_name, q, k_cache, v_cache, block_tables, context_lens, scale
         max_context_len = mbps * k_cache.shape[2]
     if scale is None:
         scale = 1.0 / math.sqrt(D)
-    need = decode_workspace_bytes(S, H, D, max_context_len, partition_size) if S else 0
+    sizer = decode_shared_workspace_bytes if fn_name == "pkv_paged_attn_decode_shared" else decode_workspace_bytes
+    need = sizer(S, H, D, max_context_len, partition_size) if S else 0
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     if workspace is not None:
@@ -143,6 +150,19 @@ def paged_attn_decode(q, k_cache, v_cache, block_tables, context_lens, scale, ou
     """
     return _decode_call("pkv_paged_attn_decode", q, k_cache, v_cache, block_tables, context_lens, scale, out,
                         max_context_len, partition_size, workspace)
+
+
+def paged_attn_decode_shared(q, k_cache, v_cache, block_tables, context_lens, scale, out, *,
+                             max_context_len=None, partition_size=DEFAULT_PARTITION, workspace=None):
+    """paged_attn_decode that reads blocks shared by neighbouring sequences once.
+
+    Same arguments and result as paged_attn_decode.  Within each window of four
+    consecutive sequences, those whose tables start with the same block ids
+    (parallel samples, a common prefix) have those blocks read once for all of
+    them.  The workspace is sized by decode_shared_workspace_bytes.
+    """
+    return _decode_call("pkv_paged_attn_decode_shared", q, k_cache, v_cache, block_tables, context_lens, scale,
+                        out, max_context_len, partition_size, workspace)
 
 
 def paged_attn_decode_partial(q, k_cache, v_cache, block_tables, context_lens, scale, out, *,
