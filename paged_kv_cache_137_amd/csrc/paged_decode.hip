@@ -176,24 +176,174 @@ __global__ __launch_bounds__(1024) void decode_plan_kernel(const DecodeArgs a) {
   }
 }
 
+// One (sequence, partition) unit of the per-sequence decode, for head h:
+// entry e of the work list.  Called by one wave; lanes as described above.
 template <typename E, typename O, int D, int BS>
-__global__ __launch_bounds__(NW * 64) void decode_partial_kernel(const DecodeArgs a) {
+__device__ __forceinline__ void private_unit(const DecodeArgs& a, int e, int h) {
   using G = DecodeGeom<E, D, BS>;
   using C = Chunk<E>;
   constexpr int VEC = G::VEC, LPT = G::LPT, TPI = G::TPI, NI = G::NI;
-
-  __shared__ int sm_unit[2];
-
   const int lane = threadIdx.x & 63;
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane / LPT;
   const int c = lane % LPT;
   const int H = a.num_heads;
-  const int HG = (H + NW - 1) / NW;  // head groups
   const int part_tokens = a.part_blocks * BS;
-  const int total = a.work_ctrl[1] * HG;
   const int64_t bstride = (int64_t)H * G::TILE;
+  const int tagged = a.work_list[e];
+  const bool reuse = tagged & 1;  // blocks shared with a neighbouring sequence
+  const int entry = tagged >> 1;
+  const int s = entry / a.num_parts;
+  const int p = entry - s * a.num_parts;
+  const int64_t sh = (int64_t)s * H + h;
+  const int ctx = clamp_ctx(a, s);
+  const int st0 = seq_start(a, s);
+  const int tok0 = st0 + p * part_tokens;
+  if (ctx <= 0) {  // undefined attention: report NaN rather than garbage
+    for (int t = lane; t < D; t += 64) Out<O>::put(a.out, sh * D + t, __builtin_nanf(""));
+    return;
+  }
+  if (tok0 >= ctx) return;
+  const int nparts = (ctx - st0 + part_tokens - 1) / part_tokens;
+  const bool direct = nparts == 1 && st0 == 0;  // the whole context is this unit's
+  const int nblk = (min(part_tokens, ctx - tok0) + BS - 1) / BS;
 
+  const uint4 qv = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(a.q) + sh * (D * G::ES) + c * 16);
+  const char* kbase = reinterpret_cast<const char*>(a.k_cache) + (int64_t)h * G::TILE + lane * 16;
+  const char* vbase = reinterpret_cast<const char*>(a.v_cache) + (int64_t)h * G::TILE + lane * 16;
+  const int32_t* trow = a.block_tables + (int64_t)s * a.max_blocks_per_seq + tok0 / BS;
+
+  float m = NEG_BIG, l = 0.f;
+  float acc[VEC];
+#pragma unroll
+  for (int e2 = 0; e2 < VEC; ++e2) acc[e2] = 0.f;
+
+
+  auto consume = [&](const uint4 (&kx)[NI], uint4 (&vx)[NI], int jb, bool bad) {
+    const int tb = tok0 + jb * BS;  // position of the block's first token
+    float sc[NI];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) sc[i] = group_sum<LPT>(C::dot(qv, kx[i])) * a.scale_log2;
+    if (tb + BS > ctx) {  // partly filled last block
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const bool dead = tb + i * TPI + r >= ctx;
+        sc[i] = dead ? -INFINITY : sc[i];
+        vx[i] = dead ? make_uint4(0u, 0u, 0u, 0u) : vx[i];
+      }
+    }
+    if (bad) {
+#pragma unroll
+      for (int i = 0; i < NI; ++i) sc[i] = __builtin_nanf("");
+    }
+    float mx = m;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) mx = fmaxf(mx, sc[i]);
+    const float alpha = fast_exp2(m - mx);
+    m = mx;
+    l *= alpha;
+#pragma unroll
+    for (int e2 = 0; e2 < VEC; ++e2) acc[e2] *= alpha;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const float pi = fast_exp2(sc[i] - m);
+      l += pi;
+      float vf[VEC];
+      C::unpack(vx[i], vf);
+#pragma unroll
+      for (int e2 = 0; e2 < VEC; ++e2) acc[e2] = fmaf(pi, vf[e2], acc[e2]);
+    }
+  };
+
+  // The whole stream is instantiated once per load kind, so that the choice
+  // is made once per unit and the loop bodies stay straight-line.
+  auto run = [&](auto nt_c) {
+    constexpr bool NTL = decltype(nt_c)::value;
+    auto load = [&](int phys, uint4 (&kx)[NI], uint4 (&vx)[NI]) {
+      const char* kp = kbase + (int64_t)phys * bstride;
+      const char* vp = vbase + (int64_t)phys * bstride;
+#pragma unroll
+      for (int i = 0; i < NI; ++i) kx[i] = load_kv16<NTL>(kp + i * 1024);
+#pragma unroll
+      for (int i = 0; i < NI; ++i) vx[i] = load_kv16<NTL>(vp + i * 1024);
+    };
+    for (int cb = 0; cb < nblk; cb += 64) {
+      const int cn = min(64, nblk - cb);
+      // The chunk's table entries, one per lane; a wave-uniform readlane picks each.
+      const int tv = lane < cn ? trow[cb + lane] : 0;
+      auto phys_of = [&](int j, bool& bad) {
+        const int ph = __builtin_amdgcn_readlane(tv, j);
+        bad = (uint64_t)(uint32_t)ph >= (uint64_t)a.num_blocks;
+        return bad ? 0 : ph;
+      };
+      int j = 0;
+      if constexpr (G::PINGPONG) {
+        uint4 kA[NI], vA[NI], kB[NI], vB[NI];
+        bool badA, badB;
+        load(phys_of(j, badA), kA, vA);
+        while (j + 2 < cn) {
+          load(phys_of(j + 1, badB), kB, vB);
+          consume(kA, vA, cb + j, badA);
+          load(phys_of(j + 2, badA), kA, vA);
+          consume(kB, vB, cb + j + 1, badB);
+          j += 2;
+        }
+        if (j + 1 < cn) {
+          load(phys_of(j + 1, badB), kB, vB);
+          consume(kA, vA, cb + j, badA);
+          consume(kB, vB, cb + j + 1, badB);
+        } else {
+          consume(kA, vA, cb + j, badA);
+        }
+      } else {
+        for (; j < cn; ++j) {
+          uint4 kA[NI], vA[NI];
+          bool badA;
+          load(phys_of(j, badA), kA, vA);
+          consume(kA, vA, cb + j, badA);
+        }
+      }
+    }
+  };
+  if (reuse) run(std::false_type{});
+  else run(std::true_type{});
+
+  // Merge the wave's TPI token rows (lanes c, c + LPT, ... hold the same
+  // dims): common maximum, rescaled sums, in a fixed butterfly order.
+  float M = m;
+#pragma unroll
+  for (int sft = LPT; sft < 64; sft <<= 1) M = fmaxf(M, __shfl_xor(M, sft, 64));
+  const float f = fast_exp2(m - M);
+  float Ls = l * f;
+#pragma unroll
+  for (int e2 = 0; e2 < VEC; ++e2) acc[e2] *= f;
+#pragma unroll
+  for (int sft = LPT; sft < 64; sft <<= 1) {
+    Ls += __shfl_xor(Ls, sft, 64);
+#pragma unroll
+    for (int e2 = 0; e2 < VEC; ++e2) acc[e2] += __shfl_xor(acc[e2], sft, 64);
+  }
+  if (r == 0) {
+    if (direct) {
+#pragma unroll
+      for (int e2 = 0; e2 < VEC; ++e2) Out<O>::put(a.out, sh * D + c * VEC + e2, acc[e2] / Ls);
+    } else {
+      const int64_t pi = sh * a.num_parts + p;
+      float* dst = a.ws_acc + pi * D + c * VEC;
+#pragma unroll
+      for (int e2 = 0; e2 < VEC; e2 += 4)
+        *reinterpret_cast<float4*>(dst + e2) = make_float4(acc[e2], acc[e2 + 1], acc[e2 + 2], acc[e2 + 3]);
+      if (c == 0) *reinterpret_cast<float2*>(a.ws_ml + pi * 2) = make_float2(M, Ls);
+    }
+  }
+}
+
+template <typename E, typename O, int D, int BS>
+__global__ __launch_bounds__(NW * 64) void decode_partial_kernel(const DecodeArgs a) {
+  __shared__ int sm_unit[2];
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int H = a.num_heads;
+  const int HG = (H + NW - 1) / NW;  // head groups
+  const int total = a.work_ctrl[1] * HG;
   for (int it = 0;; ++it) {
     // Claim the next unit; the slot alternates so one barrier suffices.
     if (threadIdx.x == 0) sm_unit[it & 1] = atomicAdd(&a.work_ctrl[0], 1);
@@ -202,153 +352,7 @@ __global__ __launch_bounds__(NW * 64) void decode_partial_kernel(const DecodeArg
     if (u >= total) break;
     const int e = u / HG;
     const int h = (u - e * HG) * NW + w;
-    if (h >= H) continue;  // a partial last head group
-    const int tagged = a.work_list[e];
-    const bool reuse = tagged & 1;  // blocks shared with a neighbouring sequence
-    const int entry = tagged >> 1;
-    const int s = entry / a.num_parts;
-    const int p = entry - s * a.num_parts;
-    const int64_t sh = (int64_t)s * H + h;
-    const int ctx = clamp_ctx(a, s);
-    const int st0 = seq_start(a, s);
-    const int tok0 = st0 + p * part_tokens;
-    if (ctx <= 0) {  // undefined attention: report NaN rather than garbage
-      for (int t = lane; t < D; t += 64) Out<O>::put(a.out, sh * D + t, __builtin_nanf(""));
-      continue;
-    }
-    if (tok0 >= ctx) continue;
-    const int nparts = (ctx - st0 + part_tokens - 1) / part_tokens;
-    const bool direct = nparts == 1 && st0 == 0;  // the whole context is this unit's
-    const int nblk = (min(part_tokens, ctx - tok0) + BS - 1) / BS;
-
-    const uint4 qv = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(a.q) + sh * (D * G::ES) + c * 16);
-    const char* kbase = reinterpret_cast<const char*>(a.k_cache) + (int64_t)h * G::TILE + lane * 16;
-    const char* vbase = reinterpret_cast<const char*>(a.v_cache) + (int64_t)h * G::TILE + lane * 16;
-    const int32_t* trow = a.block_tables + (int64_t)s * a.max_blocks_per_seq + tok0 / BS;
-
-    float m = NEG_BIG, l = 0.f;
-    float acc[VEC];
-#pragma unroll
-    for (int e2 = 0; e2 < VEC; ++e2) acc[e2] = 0.f;
-
-
-    auto consume = [&](const uint4 (&kx)[NI], uint4 (&vx)[NI], int jb, bool bad) {
-      const int tb = tok0 + jb * BS;  // position of the block's first token
-      float sc[NI];
-#pragma unroll
-      for (int i = 0; i < NI; ++i) sc[i] = group_sum<LPT>(C::dot(qv, kx[i])) * a.scale_log2;
-      if (tb + BS > ctx) {  // partly filled last block
-#pragma unroll
-        for (int i = 0; i < NI; ++i) {
-          const bool dead = tb + i * TPI + r >= ctx;
-          sc[i] = dead ? -INFINITY : sc[i];
-          vx[i] = dead ? make_uint4(0u, 0u, 0u, 0u) : vx[i];
-        }
-      }
-      if (bad) {
-#pragma unroll
-        for (int i = 0; i < NI; ++i) sc[i] = __builtin_nanf("");
-      }
-      float mx = m;
-#pragma unroll
-      for (int i = 0; i < NI; ++i) mx = fmaxf(mx, sc[i]);
-      const float alpha = fast_exp2(m - mx);
-      m = mx;
-      l *= alpha;
-#pragma unroll
-      for (int e2 = 0; e2 < VEC; ++e2) acc[e2] *= alpha;
-#pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        const float pi = fast_exp2(sc[i] - m);
-        l += pi;
-        float vf[VEC];
-        C::unpack(vx[i], vf);
-#pragma unroll
-        for (int e2 = 0; e2 < VEC; ++e2) acc[e2] = fmaf(pi, vf[e2], acc[e2]);
-      }
-    };
-
-    // The whole stream is instantiated once per load kind, so that the choice
-    // is made once per unit and the loop bodies stay straight-line.
-    auto run = [&](auto nt_c) {
-      constexpr bool NTL = decltype(nt_c)::value;
-      auto load = [&](int phys, uint4 (&kx)[NI], uint4 (&vx)[NI]) {
-        const char* kp = kbase + (int64_t)phys * bstride;
-        const char* vp = vbase + (int64_t)phys * bstride;
-#pragma unroll
-        for (int i = 0; i < NI; ++i) kx[i] = load_kv16<NTL>(kp + i * 1024);
-#pragma unroll
-        for (int i = 0; i < NI; ++i) vx[i] = load_kv16<NTL>(vp + i * 1024);
-      };
-      for (int cb = 0; cb < nblk; cb += 64) {
-        const int cn = min(64, nblk - cb);
-        // The chunk's table entries, one per lane; a wave-uniform readlane picks each.
-        const int tv = lane < cn ? trow[cb + lane] : 0;
-        auto phys_of = [&](int j, bool& bad) {
-          const int ph = __builtin_amdgcn_readlane(tv, j);
-          bad = (uint64_t)(uint32_t)ph >= (uint64_t)a.num_blocks;
-          return bad ? 0 : ph;
-        };
-        int j = 0;
-        if constexpr (G::PINGPONG) {
-          uint4 kA[NI], vA[NI], kB[NI], vB[NI];
-          bool badA, badB;
-          load(phys_of(j, badA), kA, vA);
-          while (j + 2 < cn) {
-            load(phys_of(j + 1, badB), kB, vB);
-            consume(kA, vA, cb + j, badA);
-            load(phys_of(j + 2, badA), kA, vA);
-            consume(kB, vB, cb + j + 1, badB);
-            j += 2;
-          }
-          if (j + 1 < cn) {
-            load(phys_of(j + 1, badB), kB, vB);
-            consume(kA, vA, cb + j, badA);
-            consume(kB, vB, cb + j + 1, badB);
-          } else {
-            consume(kA, vA, cb + j, badA);
-          }
-        } else {
-          for (; j < cn; ++j) {
-            uint4 kA[NI], vA[NI];
-            bool badA;
-            load(phys_of(j, badA), kA, vA);
-            consume(kA, vA, cb + j, badA);
-          }
-        }
-      }
-    };
-    if (reuse) run(std::false_type{});
-    else run(std::true_type{});
-
-    // Merge the wave's TPI token rows (lanes c, c + LPT, ... hold the same
-    // dims): common maximum, rescaled sums, in a fixed butterfly order.
-    float M = m;
-#pragma unroll
-    for (int sft = LPT; sft < 64; sft <<= 1) M = fmaxf(M, __shfl_xor(M, sft, 64));
-    const float f = fast_exp2(m - M);
-    float Ls = l * f;
-#pragma unroll
-    for (int e2 = 0; e2 < VEC; ++e2) acc[e2] *= f;
-#pragma unroll
-    for (int sft = LPT; sft < 64; sft <<= 1) {
-      Ls += __shfl_xor(Ls, sft, 64);
-#pragma unroll
-      for (int e2 = 0; e2 < VEC; ++e2) acc[e2] += __shfl_xor(acc[e2], sft, 64);
-    }
-    if (r == 0) {
-      if (direct) {
-#pragma unroll
-        for (int e2 = 0; e2 < VEC; ++e2) Out<O>::put(a.out, sh * D + c * VEC + e2, acc[e2] / Ls);
-      } else {
-        const int64_t pi = sh * a.num_parts + p;
-        float* dst = a.ws_acc + pi * D + c * VEC;
-#pragma unroll
-        for (int e2 = 0; e2 < VEC; e2 += 4)
-          *reinterpret_cast<float4*>(dst + e2) = make_float4(acc[e2], acc[e2 + 1], acc[e2 + 2], acc[e2 + 3]);
-        if (c == 0) *reinterpret_cast<float2*>(a.ws_ml + pi * 2) = make_float2(M, Ls);
-      }
-    }
+    if (h < H) private_unit<E, O, D, BS>(a, e, h);  // else a partial last head group
   }
 }
 
@@ -390,10 +394,11 @@ __global__ __launch_bounds__(D) void decode_reduce_kernel(const DecodeArgs a) {
 // members are the window's sequences whose first block id is the leader's.
 // J is the number of leading full blocks that every member holds with the
 // leader's ids, all inside every member's context.  A window with two or more
-// members and J >= 1 is a group: decode_group_kernel reads its J blocks once,
-// in partitions, and writes one partial result per member; each member then
-// attends to tokens J*BS .. ctx-1 on its own (decode_partial_kernel, with
-// tok_start), and the reduce merges both kinds of partial results.
+// members and J >= 1 is a group.  decode_shared_kernel reads a group's J
+// blocks once, in partitions (group units), writing one partial result per
+// member, and runs each member's tokens J*BS .. ctx-1 as ordinary
+// per-sequence units (tok_start); the reduce merges both kinds of partial
+// results.
 
 // One wave per window.
 __global__ __launch_bounds__(1024) void share_detect_kernel(const DecodeArgs a) {
@@ -452,170 +457,163 @@ __global__ __launch_bounds__(1024) void share_detect_kernel(const DecodeArgs a) 
   if (lane < GW && s0 + lane < a.num_seqs) a.tok_start[s0 + lane] = grp && ((mask >> lane) & 1) ? J * BS : 0;
 }
 
-// Persistent kernel over (window, partition of the shared blocks, NW heads)
-// units.  Wave w streams head NW*g + w of the group's shared blocks once and
-// keeps one online softmax per member (its own query), with the same lane
-// layout as decode_partial_kernel.  Every shared block is full and inside
-// every member's context, so no slot is masked.
+// One group unit: entry e = (window, partition of the shared blocks), head h.
+// The wave streams head h of the group's shared blocks once and keeps one
+// online softmax per member (its own query), with the same lane layout as
+// decode_partial_kernel.  Every shared block is full and inside every
+// member's context, so no slot is masked.
 template <typename E, typename O, int D, int BS>
-__global__ __launch_bounds__(NW * 64) void decode_group_kernel(const DecodeArgs a) {
+__device__ __forceinline__ void group_unit(const DecodeArgs& a, int e, int h) {
   using G = DecodeGeom<E, D, BS>;
   using C = Chunk<E>;
   constexpr int VEC = G::VEC, LPT = G::LPT, NI = G::NI;
   constexpr int GW = SHARE_WINDOW;
-
-  __shared__ int sm_unit[2];
-
   const int lane = threadIdx.x & 63;
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane / LPT;
   const int c = lane % LPT;
   const int H = a.num_heads;
-  const int HG = (H + NW - 1) / NW;
   const int part_tokens = a.part_blocks * BS;
-  const int total = a.num_windows * a.num_parts * HG;
   const int64_t bstride = (int64_t)H * G::TILE;
+  const int win = e / a.num_parts;
+  const int p = e - win * a.num_parts;
+  const int info = __builtin_amdgcn_readfirstlane(a.win_info[win]);
+  if (info == 0) return;
+  const int J = info >> 4, mask = info & 15;
+  const int tok0 = p * part_tokens;
+  const int tend = min(tok0 + part_tokens, J * BS);
+  if (tok0 >= tend) return;
+  const int nblk = (tend - tok0) / BS;
+  const int s0 = win * GW;
 
-  for (int it = 0;; ++it) {
-    if (threadIdx.x == 0) sm_unit[it & 1] = atomicAdd(&a.work_ctrl[2], 1);
-    __syncthreads();
-    const int u = __builtin_amdgcn_readfirstlane(sm_unit[it & 1]);
-    if (u >= total) break;
-    const int e = u / HG;
-    const int h = (u - e * HG) * NW + w;
-    if (h >= H) continue;
-    const int win = e / a.num_parts;
-    const int p = e - win * a.num_parts;
-    const int info = __builtin_amdgcn_readfirstlane(a.win_info[win]);
-    if (info == 0) continue;
-    const int J = info >> 4, mask = info & 15;
-    const int tok0 = p * part_tokens;
-    const int tend = min(tok0 + part_tokens, J * BS);
-    if (tok0 >= tend) continue;
-    const int nblk = (tend - tok0) / BS;
-    const int s0 = win * GW;
+  uint4 qv[GW];
+  float m[GW], l[GW], acc[GW][VEC];
+#pragma unroll
+  for (int i = 0; i < GW; ++i) {
+    qv[i] = make_uint4(0u, 0u, 0u, 0u);
+    if ((mask >> i) & 1)
+      qv[i] = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(a.q) +
+                                              ((int64_t)(s0 + i) * H + h) * (D * G::ES) + c * 16);
+    m[i] = NEG_BIG;
+    l[i] = 0.f;
+#pragma unroll
+    for (int e2 = 0; e2 < VEC; ++e2) acc[i][e2] = 0.f;
+  }
+  const char* kbase = reinterpret_cast<const char*>(a.k_cache) + (int64_t)h * G::TILE + lane * 16;
+  const char* vbase = reinterpret_cast<const char*>(a.v_cache) + (int64_t)h * G::TILE + lane * 16;
+  const int lead = __builtin_ctz(mask);
+  const int32_t* trow = a.block_tables + (int64_t)(s0 + lead) * a.max_blocks_per_seq + tok0 / BS;
 
-    uint4 qv[GW];
-    float m[GW], l[GW], acc[GW][VEC];
-#pragma unroll
-    for (int i = 0; i < GW; ++i) {
-      qv[i] = make_uint4(0u, 0u, 0u, 0u);
-      if ((mask >> i) & 1)
-        qv[i] = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(a.q) +
-                                                ((int64_t)(s0 + i) * H + h) * (D * G::ES) + c * 16);
-      m[i] = NEG_BIG;
-      l[i] = 0.f;
-#pragma unroll
-      for (int e2 = 0; e2 < VEC; ++e2) acc[i][e2] = 0.f;
-    }
-    const char* kbase = reinterpret_cast<const char*>(a.k_cache) + (int64_t)h * G::TILE + lane * 16;
-    const char* vbase = reinterpret_cast<const char*>(a.v_cache) + (int64_t)h * G::TILE + lane * 16;
-    const int lead = __builtin_ctz(mask);
-    const int32_t* trow = a.block_tables + (int64_t)(s0 + lead) * a.max_blocks_per_seq + tok0 / BS;
-
-    auto consume = [&](const uint4 (&kx)[NI], const uint4 (&vx)[NI], bool bad) {
-      float vf[NI][VEC];
-#pragma unroll
-      for (int i = 0; i < NI; ++i) C::unpack(vx[i], vf[i]);
-#pragma unroll
-      for (int g = 0; g < GW; ++g) {
-        if (!((mask >> g) & 1)) continue;
-        float sc[NI];
-#pragma unroll
-        for (int i = 0; i < NI; ++i) sc[i] = group_sum<LPT>(C::dot(qv[g], kx[i])) * a.scale_log2;
-        if (bad) {
-#pragma unroll
-          for (int i = 0; i < NI; ++i) sc[i] = __builtin_nanf("");
-        }
-        float mx = m[g];
-#pragma unroll
-        for (int i = 0; i < NI; ++i) mx = fmaxf(mx, sc[i]);
-        const float alpha = fast_exp2(m[g] - mx);
-        m[g] = mx;
-        l[g] *= alpha;
-#pragma unroll
-        for (int e2 = 0; e2 < VEC; ++e2) acc[g][e2] *= alpha;
-#pragma unroll
-        for (int i = 0; i < NI; ++i) {
-          const float pi = fast_exp2(sc[i] - mx);
-          l[g] += pi;
-#pragma unroll
-          for (int e2 = 0; e2 < VEC; ++e2) acc[g][e2] = fmaf(pi, vf[i][e2], acc[g][e2]);
-        }
-      }
-    };
-    auto load = [&](int phys, uint4 (&kx)[NI], uint4 (&vx)[NI]) {
-      const char* kp = kbase + (int64_t)phys * bstride;
-      const char* vp = vbase + (int64_t)phys * bstride;
-#pragma unroll
-      for (int i = 0; i < NI; ++i) kx[i] = load_kv16<true>(kp + i * 1024);
-#pragma unroll
-      for (int i = 0; i < NI; ++i) vx[i] = load_kv16<true>(vp + i * 1024);
-    };
-    for (int cb = 0; cb < nblk; cb += 64) {
-      const int cn = min(64, nblk - cb);
-      const int tv = lane < cn ? trow[cb + lane] : 0;
-      auto phys_of = [&](int j, bool& bad) {
-        const int ph = __builtin_amdgcn_readlane(tv, j);
-        bad = (uint64_t)(uint32_t)ph >= (uint64_t)a.num_blocks;
-        return bad ? 0 : ph;
-      };
-      int j = 0;
-      if constexpr (G::PINGPONG) {
-        uint4 kA[NI], vA[NI], kB[NI], vB[NI];
-        bool badA, badB;
-        load(phys_of(j, badA), kA, vA);
-        while (j + 2 < cn) {
-          load(phys_of(j + 1, badB), kB, vB);
-          consume(kA, vA, badA);
-          load(phys_of(j + 2, badA), kA, vA);
-          consume(kB, vB, badB);
-          j += 2;
-        }
-        if (j + 1 < cn) {
-          load(phys_of(j + 1, badB), kB, vB);
-          consume(kA, vA, badA);
-          consume(kB, vB, badB);
-        } else {
-          consume(kA, vA, badA);
-        }
-      } else {
-        for (; j < cn; ++j) {
-          uint4 kA[NI], vA[NI];
-          bool badA;
-          load(phys_of(j, badA), kA, vA);
-          consume(kA, vA, badA);
-        }
-      }
-    }
-
-    // Per member: merge the wave's token rows, then store the partial result.
+  auto consume = [&](const uint4 (&kx)[NI], const uint4 (&vx)[NI], bool bad) {
 #pragma unroll
     for (int g = 0; g < GW; ++g) {
       if (!((mask >> g) & 1)) continue;
-      float M = m[g];
+      float sc[NI];
 #pragma unroll
-      for (int sft = LPT; sft < 64; sft <<= 1) M = fmaxf(M, __shfl_xor(M, sft, 64));
-      const float f = fast_exp2(m[g] - M);
-      float Ls = l[g] * f;
-      float av[VEC];
+      for (int i = 0; i < NI; ++i) sc[i] = group_sum<LPT>(C::dot(qv[g], kx[i])) * a.scale_log2;
+      if (bad) {
 #pragma unroll
-      for (int e2 = 0; e2 < VEC; ++e2) av[e2] = acc[g][e2] * f;
-#pragma unroll
-      for (int sft = LPT; sft < 64; sft <<= 1) {
-        Ls += __shfl_xor(Ls, sft, 64);
-#pragma unroll
-        for (int e2 = 0; e2 < VEC; ++e2) av[e2] += __shfl_xor(av[e2], sft, 64);
+        for (int i = 0; i < NI; ++i) sc[i] = __builtin_nanf("");
       }
-      if (r == 0) {
-        const int64_t pi = ((int64_t)(s0 + g) * H + h) * a.num_parts + p;
-        float* dst = a.ws_acc_sh + pi * D + c * VEC;
+      float mx = m[g];
 #pragma unroll
-        for (int e2 = 0; e2 < VEC; e2 += 4)
-          *reinterpret_cast<float4*>(dst + e2) = make_float4(av[e2], av[e2 + 1], av[e2 + 2], av[e2 + 3]);
-        if (c == 0) *reinterpret_cast<float2*>(a.ws_ml_sh + pi * 2) = make_float2(M, Ls);
+      for (int i = 0; i < NI; ++i) mx = fmaxf(mx, sc[i]);
+      const float alpha = fast_exp2(m[g] - mx);
+      m[g] = mx;
+      l[g] *= alpha;
+#pragma unroll
+      for (int e2 = 0; e2 < VEC; ++e2) acc[g][e2] *= alpha;
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const float pi = fast_exp2(sc[i] - mx);
+        l[g] += pi;
+        float vf[VEC];
+        C::unpack(vx[i], vf);
+#pragma unroll
+        for (int e2 = 0; e2 < VEC; ++e2) acc[g][e2] = fmaf(pi, vf[e2], acc[g][e2]);
       }
     }
+  };
+  auto load = [&](int phys, uint4 (&kx)[NI], uint4 (&vx)[NI]) {
+    const char* kp = kbase + (int64_t)phys * bstride;
+    const char* vp = vbase + (int64_t)phys * bstride;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) kx[i] = load_kv16<true>(kp + i * 1024);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) vx[i] = load_kv16<true>(vp + i * 1024);
+  };
+  for (int cb = 0; cb < nblk; cb += 64) {
+    const int cn = min(64, nblk - cb);
+    const int tv = lane < cn ? trow[cb + lane] : 0;
+    auto phys_of = [&](int j, bool& bad) {
+      const int ph = __builtin_amdgcn_readlane(tv, j);
+      bad = (uint64_t)(uint32_t)ph >= (uint64_t)a.num_blocks;
+      return bad ? 0 : ph;
+    };
+    int j = 0;
+    // One tile in flight: the members' accumulators take the registers a
+    // second set would need, and the kernel keeps the occupancy of the
+    // per-sequence units it shares.
+    for (; j < cn; ++j) {
+      uint4 kA[NI], vA[NI];
+      bool badA;
+      load(phys_of(j, badA), kA, vA);
+      consume(kA, vA, badA);
+    }
+  }
+
+  // Per member: merge the wave's token rows, then store the partial result.
+#pragma unroll
+  for (int g = 0; g < GW; ++g) {
+    if (!((mask >> g) & 1)) continue;
+    float M = m[g];
+#pragma unroll
+    for (int sft = LPT; sft < 64; sft <<= 1) M = fmaxf(M, __shfl_xor(M, sft, 64));
+    const float f = fast_exp2(m[g] - M);
+    float Ls = l[g] * f;
+    float av[VEC];
+#pragma unroll
+    for (int e2 = 0; e2 < VEC; ++e2) av[e2] = acc[g][e2] * f;
+#pragma unroll
+    for (int sft = LPT; sft < 64; sft <<= 1) {
+      Ls += __shfl_xor(Ls, sft, 64);
+#pragma unroll
+      for (int e2 = 0; e2 < VEC; ++e2) av[e2] += __shfl_xor(av[e2], sft, 64);
+    }
+    if (r == 0) {
+      const int64_t pi = ((int64_t)(s0 + g) * H + h) * a.num_parts + p;
+      float* dst = a.ws_acc_sh + pi * D + c * VEC;
+#pragma unroll
+      for (int e2 = 0; e2 < VEC; e2 += 4)
+        *reinterpret_cast<float4*>(dst + e2) = make_float4(av[e2], av[e2 + 1], av[e2 + 2], av[e2 + 3]);
+      if (c == 0) *reinterpret_cast<float2*>(a.ws_ml_sh + pi * 2) = make_float2(M, Ls);
+    }
+  }
+}
+
+// Persistent kernel of the shared-prefix form: the group units (window,
+// partition of the shared blocks, NW heads) first, then the per-sequence
+// units of the plan's list, claimed from one counter, so that the two kinds
+// fill each other's gaps.
+template <typename E, typename O, int D, int BS>
+__global__ __launch_bounds__(NW * 64) void decode_shared_kernel(const DecodeArgs a) {
+  __shared__ int sm_unit[2];
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int H = a.num_heads;
+  const int HG = (H + NW - 1) / NW;
+  const int ng = a.num_windows * a.num_parts * HG;
+  const int total = ng + a.work_ctrl[1] * HG;
+  for (int it = 0;; ++it) {
+    if (threadIdx.x == 0) sm_unit[it & 1] = atomicAdd(&a.work_ctrl[0], 1);
+    __syncthreads();
+    int u = __builtin_amdgcn_readfirstlane(sm_unit[it & 1]);
+    if (u >= total) break;
+    const bool grp = u < ng;
+    if (!grp) u -= ng;
+    const int e = u / HG;
+    const int h = (u - e * HG) * NW + w;
+    if (h >= H) continue;  // a partial last head group
+    if (grp) group_unit<E, O, D, BS>(a, e, h);
+    else private_unit<E, O, D, BS>(a, e, h);
   }
 }
 
@@ -728,11 +726,9 @@ template <typename E, typename O, int D, int BS>
 static hipError_t shared_bs(const DecodeArgs& a, hipStream_t st) {
   hipLaunchKernelGGL(share_detect_kernel, dim3((a.num_windows + 15) / 16), dim3(1024), 0, st, a);
   hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(1024), 0, st, a);
-  const int64_t gunits = (int64_t)a.num_windows * a.num_parts * ((a.num_heads + NW - 1) / NW);
-  const int ggrid = persistent_grid<decode_group_kernel<E, O, D, BS>>(NW * 64, gunits);
-  hipLaunchKernelGGL((decode_group_kernel<E, O, D, BS>), dim3(ggrid), dim3(NW * 64), 0, st, a);
-  const int grid = persistent_grid<decode_partial_kernel<E, O, D, BS>>(NW * 64, ((int64_t)a.total_units + NW - 1) / NW);
-  hipLaunchKernelGGL((decode_partial_kernel<E, O, D, BS>), dim3(grid), dim3(NW * 64), 0, st, a);
+  const int64_t units = ((int64_t)a.num_windows * a.num_parts + a.total_units) * ((a.num_heads + NW - 1) / NW);
+  const int grid = persistent_grid<decode_shared_kernel<E, O, D, BS>>(NW * 64, units);
+  hipLaunchKernelGGL((decode_shared_kernel<E, O, D, BS>), dim3(grid), dim3(NW * 64), 0, st, a);
   return hipGetLastError();
 }
 
