@@ -54,7 +54,8 @@ def build_library(jobs: int | None = None) -> str:
     with ThreadPoolExecutor(jobs) as ex:
         list(ex.map(lambda so: _run([HIPCC, *CFLAGS, "-c", so[0], "-o", so[1]]), zip(srcs, objs)))
     tmp = LIB + f".tmp{os.getpid()}"
-    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp])
+    # --no-undefined: a kernel whose host stub went missing fails the build, not the load.
+    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Wl,--no-undefined", *objs, "-o", tmp])
     os.replace(tmp, LIB)
     return LIB
 

@@ -58,6 +58,23 @@ namespace pkv {
 // Buffer resource word 3 for gfx9-family parts: raw (untyped) 32-bit dword access.
 constexpr int BUF_RSRC_WORD3 = 0x00020000;
 
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// 64 lanes x 16 bytes from a buffer straight into LDS: lane l's bytes land at
+// lds + 16*l (lds is wave-uniform).
+__device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voffset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds, 16, voffset, 0, 0, 0);
+}
+// ds_read_b64_tr_b16: in each group of 16 lanes, lane i addresses 4 16-bit
+// values (row i of a 16 x 4 matrix M); lane j receives M[j/4 + 4k][j%4], k = 0..3.
+__device__ __forceinline__ uint2 lds_read_tr16(const void* p) {
+  return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4i16_t*)(lds_ptr_t)p));
+}
+// Wait for this wave's outstanding vector-memory operations (loads into LDS included).
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 template <typename E>
 __device__ __forceinline__ f32x16_t mfma32(const uint4& a, const uint4& b, const f32x16_t& c);
 template <>
@@ -150,9 +167,28 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
   constexpr int VG = (BN / 4) * (D / 8);   // (4 keys x 8 dims) V groups per tile
   constexpr float RESCALE_SLACK = 8.0f;    // log2 units a row maximum may rise before rescaling
   static_assert(KCH * 256 == BN * (D / 8) && VG <= 256, "staging must map onto 256 threads");
-  // Two LDS buffers: tile n is read from one while tile n+1 is written to the other.
-  __shared__ __attribute__((aligned(16))) unsigned char k_lds[2][BN * KROW];
-  __shared__ __attribute__((aligned(16))) unsigned char v_lds[2][D * VROW];
+  // Two LDS buffers per tensor: tile n is read from one while tile n+1 is
+  // written to the other.  Separate objects, so the compiler can tell a
+  // pending direct-to-LDS load into one from reads of the other.
+  //  - Fresh prompt (PB = 0): K and V tiles row-major [key][dim], dense
+  //    (2*D bytes per row), filled by buffer loads straight into LDS.  The
+  //    16-byte chunks of each row are XOR-swizzled by the row index, so
+  //    that the fragment reads below touch every bank evenly.
+  //  - Paged (PB > 0): K row-major padded to KROW bytes, V transposed to
+  //    [dim][key] padded to VROW bytes, both staged through registers.
+  constexpr int ROWB = D * 2;                        // bytes of one dense row
+  constexpr int CPR = ROWB / 16;                     // 16-byte chunks per dense row
+  constexpr int KBUF = PAGED ? BN * KROW : BN * ROWB;
+  constexpr int VBUF = PAGED ? D * VROW : BN * ROWB;
+  __shared__ __attribute__((aligned(1024))) unsigned char k_lds0[KBUF], k_lds1[KBUF];
+  __shared__ __attribute__((aligned(1024))) unsigned char v_lds0[VBUF], v_lds1[VBUF];
+  auto kbuf = [&](int b) -> unsigned char* { return b ? k_lds1 : k_lds0; };
+  auto vbuf = [&](int b) -> unsigned char* { return b ? v_lds1 : v_lds0; };
+  // Swizzled chunk of a dense row: K's fragment reads take one 16-byte chunk
+  // from each of 16 consecutive rows, V's transposing reads take 8 bytes from
+  // each of 8 consecutive rows in runs of 4 chunks.
+  auto kswz = [](int row, int c) { return D == 128 ? c ^ (row & 15) : c ^ ((row >> 1) & 7); };
+  auto vswz = [](int row, int c) { return D == 128 ? c ^ (4 * (row & 3)) : c ^ (4 * ((row >> 1) & 1)); };
 
   // Work item w enumerates (head, prompt, query tile), tile fastest and longest
   // first.  With the XCD remap, each XCD walks a contiguous range of w.  All
@@ -256,7 +292,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
     }
   };
   load_ids(0);
-  auto gload = [&](Stage& st_, int n0) {
+  auto gload = [&](Stage& st_, int n0) __attribute__((always_inline)) {
     uint4 (&kst)[KCH] = st_.k;
     uint4 (&vst)[4] = st_.v;
     if constexpr (PAGED) {
@@ -310,11 +346,11 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
     }
   };
   // K row-major [key][dim]; V transposed to [dim][key], 4 keys per 8-byte store.
-  auto lstore = [&](const Stage& st_, int buf) {
+  auto lstore = [&](const Stage& st_, int buf) __attribute__((always_inline)) {
     const uint4 (&kst)[KCH] = st_.k;
     const uint4 (&vst)[4] = st_.v;
 #pragma unroll
-    for (int i = 0; i < KCH; ++i) *reinterpret_cast<uint4*>(k_lds[buf] + klds[i]) = kst[i];
+    for (int i = 0; i < KCH; ++i) *reinterpret_cast<uint4*>(kbuf(buf) + klds[i]) = kst[i];
     if (threadIdx.x < VG) {
       const uint32_t w0[4] = {vst[0].x, vst[0].y, vst[0].z, vst[0].w};
       const uint32_t w1[4] = {vst[1].x, vst[1].y, vst[1].z, vst[1].w};
@@ -328,10 +364,41 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
                                       __builtin_amdgcn_perm(w3[qd], w2[qd], 0x05040100u));
         const uint2 odd = make_uint2(__builtin_amdgcn_perm(w1[qd], w0[qd], 0x07060302u),
                                      __builtin_amdgcn_perm(w3[qd], w2[qd], 0x07060302u));
-        *reinterpret_cast<uint2*>(v_lds[buf] + vlds + (2 * qd) * VROW) = even;
-        *reinterpret_cast<uint2*>(v_lds[buf] + vlds + (2 * qd + 1) * VROW) = odd;
+        *reinterpret_cast<uint2*>(vbuf(buf) + vlds + (2 * qd) * VROW) = even;
+        *reinterpret_cast<uint2*>(vbuf(buf) + vlds + (2 * qd + 1) * VROW) = odd;
       }
     }
+  };
+
+  // Fresh prompt: the tile at key n0 straight from HBM into LDS buffer b.
+  // Each wave instruction fills one 1 KiB run of the dense tile (RPI rows):
+  // lane l lands at byte 16*l of the run, so it loads the logical chunk that
+  // the swizzle puts there.  Rows at or past the prompt end lie at or beyond
+  // num_records and are written as zeros.
+  auto gdma = [&](int n0, int b) __attribute__((always_inline)) {
+    if constexpr (!PAGED) {
+      constexpr int RPI = 1024 / ROWB;   // rows per wave instruction
+      constexpr int IPW = BN / RPI / 4;  // instructions per wave per tensor
+      const int rows = min(L - n0, BN);  // >= 1: n0 < L here
+      const int nrec = (rows - 1) * (int)rsb + D * 2;
+      const __amdgpu_buffer_rsrc_t rk =
+          __builtin_amdgcn_make_buffer_rsrc((void*)(kb + (int64_t)n0 * rsb), (short)0, nrec, BUF_RSRC_WORD3);
+      const __amdgpu_buffer_rsrc_t rv =
+          __builtin_amdgcn_make_buffer_rsrc((void*)(vb + (int64_t)n0 * rsb), (short)0, nrec, BUF_RSRC_WORD3);
+#pragma unroll
+      for (int j = 0; j < IPW; ++j) {
+        const int blk = w * IPW + j;
+        const int row = blk * RPI + lane / CPR;
+        const int pc = lane % CPR;
+        buffer_load_lds16(rk, kbuf(b) + blk * 1024, row * rsb + kswz(row, pc) * 16);
+        buffer_load_lds16(rv, vbuf(b) + blk * 1024, row * rsb + vswz(row, pc) * 16);
+      }
+    }
+  };
+  // The loads into LDS above complete asynchronously: wait for this wave's
+  // before the barrier that publishes the tile.
+  auto dma_wait = [&]() {
+    if constexpr (!PAGED) wait_vmem();
   };
 
   f32x16_t o[DB];
@@ -357,7 +424,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
   // lane-local partial row sum against a shared reference maximum mrow.  They
   // exchange values only when mrow must move: when some row's maximum rises by
   // more than the slack.
-  auto tile = [&](auto masked_c, int buf, int n0) {
+  auto tile = [&](auto masked_c, int buf, int n0) __attribute__((always_inline)) {
     constexpr bool MASKED = decltype(masked_c)::value;
     f32x16_t st[2];
 #pragma unroll
@@ -368,8 +435,10 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
     for (int kk = 0; kk < KS; ++kk)
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        const unsigned char* kr = k_lds[buf] + (u * 32 + ql) * KROW + hf * 16;
-        st[u] = mfma32<E>(*reinterpret_cast<const uint4*>(kr + kk * 32), qf[kk], st[u]);
+        const int row = u * 32 + ql;
+        const unsigned char* kr = PAGED ? kbuf(buf) + row * KROW + (2 * kk + hf) * 16
+                                        : kbuf(buf) + row * ROWB + kswz(row, 2 * kk + hf) * 16;
+        st[u] = mfma32<E>(*reinterpret_cast<const uint4*>(kr), qf[kk], st[u]);
       }
 
     if constexpr (MASKED) {
@@ -416,9 +485,23 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
         const int kb0 = u * 32 + 16 * kk2 + 4 * hf;  // key within the LDS tile
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          const unsigned char* vr = v_lds[buf] + (db * 32 + ql) * VROW;
-          const uint2 lo = *reinterpret_cast<const uint2*>(vr + kb0 * 2);
-          const uint2 hi = *reinterpret_cast<const uint2*>(vr + (kb0 + 8) * 2);
+          uint2 lo, hi;
+          if constexpr (PAGED) {
+            const unsigned char* vr = vbuf(buf) + (db * 32 + ql) * VROW;
+            lo = *reinterpret_cast<const uint2*>(vr + kb0 * 2);
+            hi = *reinterpret_cast<const uint2*>(vr + (kb0 + 8) * 2);
+          } else {
+            // Transposing reads (ds_read_b64_tr_b16): in each group of 16
+            // lanes, lane i points at 4 values of row kb0 + i/4, dims
+            // d0 + 4*(i%4); lane j then receives dim d0 + j of rows kb0 .. kb0+3.
+            const int i16 = ql & 15;
+            const int dim = db * 32 + (ql & 16) + 4 * (i16 & 3);
+            auto tr = [&](int row) __attribute__((always_inline)) {
+              return lds_read_tr16(vbuf(buf) + row * ROWB + vswz(row, dim >> 3) * 16 + (dim & 7) * 2);
+            };
+            lo = tr(kb0 + (i16 >> 2));
+            hi = tr(kb0 + 8 + (i16 >> 2));
+          }
           o[db] = mfma32<E>(make_uint4(lo.x, lo.y, hi.x, hi.y), pb, o[db]);
         }
       }
@@ -430,24 +513,42 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
   // tile that lies wholly in its queries' future.
   const int ntiles = (kend + BN - 1) / BN;
   const int nfull = min((C + m0) / BN, ntiles);
-  gload(sa, 0);
-  lstore(sa, 0);
-  __syncthreads();
-  int buf = 0;
+  // Stage tile t+1 while tile t is multiplied: through registers (paged) or
+  // straight into LDS (fresh prompt); one barrier per tile.
+  auto stage = [&](int n0, int b) __attribute__((always_inline)) {
+    if constexpr (PAGED) gload(sa, n0);
+    else gdma(n0, b);
+  };
+  auto publish = [&](bool more, int b) __attribute__((always_inline)) {
+    if constexpr (PAGED) {
+      if (more) lstore(sa, b);
+    } else {
+      dma_wait();
+    }
+    __syncthreads();
+  };
+  stage(0, 0);
+  publish(true, 0);
+  // Steps are unrolled in pairs, so that every LDS address names its buffer
+  // at compile time (the compiler then sees that a load into one buffer and
+  // the reads of the other do not overlap).
+  auto step = [&](auto masked_c, auto buf_c, int t) __attribute__((always_inline)) {
+    constexpr int b = decltype(buf_c)::value;
+    const bool more = t + 1 < ntiles;
+    if (more) stage((t + 1) * BN, b ^ 1);
+    if (!decltype(masked_c)::value || t * BN < wkend) tile(masked_c, b, t * BN);
+    publish(more, b ^ 1);
+  };
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
   int tt = 0;
-  for (; tt < nfull; ++tt, buf ^= 1) {
-    const bool more = tt + 1 < ntiles;
-    if (more) gload(sa, (tt + 1) * BN);
-    tile(std::false_type(), buf, tt * BN);
-    if (more) lstore(sa, buf ^ 1);
-    __syncthreads();
+  for (; tt + 1 < nfull; tt += 2) {
+    step(std::false_type(), B0(), tt);
+    step(std::false_type(), B1(), tt + 1);
   }
-  for (; tt < ntiles; ++tt, buf ^= 1) {
-    const bool more = tt + 1 < ntiles;
-    if (more) gload(sa, (tt + 1) * BN);
-    if (tt * BN < wkend) tile(std::true_type(), buf, tt * BN);
-    if (more) lstore(sa, buf ^ 1);
-    __syncthreads();
+  for (; tt < ntiles; tt += 2) {
+    step(std::true_type(), B0(), tt);
+    if (tt + 1 < ntiles) step(std::true_type(), B1(), tt + 1);
   }
   lrow += __shfl_xor(lrow, 32, 64);  // the two halves' partial row sums
 
