@@ -151,44 +151,33 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
   constexpr bool PAGED = PB != 0;
   constexpr int SH = PB == 8 ? 3 : PB == 16 ? 4 : PB == 32 ? 5 : 0;  // log2 of the block size
   static_assert(!PAGED || (1 << SH) == PB, "block size 8, 16 or 32");
-  // A wave's 16-byte K chunks of one staging slot cover 512 / D consecutive
-  // rows starting at a multiple of that count, so they sit in one block.
-  static_assert(!PAGED || 512 / D <= PB, "a wave's K rows must share a block");
-  // Two quiet NaNs of the element type, packed: the value of a tile whose
-  // block id lies outside the pool.
-  constexpr uint32_t E16_NAN2 = std::is_same<E, bf16_t>::value ? 0x7fc07fc0u : 0x7e007e00u;
-  constexpr int BM = PREFILL_BLOCK_M;      // query rows per workgroup (4 waves x 32)
-  constexpr int BN = 64;                   // keys per LDS tile
-  constexpr int KS = D / 16;               // k-steps of Q K^T
-  constexpr int DB = D / 32;               // 32-row blocks of O^T
-  constexpr int KROW = D * 2 + 16;         // LDS bytes per K row, padded against bank conflicts
-  constexpr int VROW = BN * 2 + 8;         // LDS bytes per V^T row, padded likewise
-  constexpr int KCH = BN * (D / 8) / 256;  // 16-byte K chunks each thread stages per tile
-  constexpr int VG = (BN / 4) * (D / 8);   // (4 keys x 8 dims) V groups per tile
-  constexpr float RESCALE_SLACK = 8.0f;    // log2 units a row maximum may rise before rescaling
-  static_assert(KCH * 256 == BN * (D / 8) && VG <= 256, "staging must map onto 256 threads");
+  constexpr int BM = PREFILL_BLOCK_M;  // query rows per workgroup (4 waves x 32)
+  constexpr int BN = 64;               // keys per LDS tile
+  constexpr int KS = D / 16;           // k-steps of Q K^T
+  constexpr int DB = D / 32;           // 32-row blocks of O^T
+  constexpr int ROWB = D * 2;          // bytes of one K or V row
+  constexpr int CPR = ROWB / 16;       // 16-byte chunks per row
+  constexpr int RPI = 1024 / ROWB;     // rows per 1 KiB wave load into LDS
+  constexpr int IPW = BN / RPI / 4;    // such loads per wave, per tensor and tile
+  constexpr int TILE = BN * ROWB;      // bytes of one K or V tile
+  constexpr float RESCALE_SLACK = 8.0f;  // log2 units a row maximum may rise before rescaling
+  static_assert(IPW * RPI * 4 == BN, "a tile must map onto 4 waves of 1 KiB loads");
+  static_assert(!PAGED || RPI <= PB, "a 1 KiB run of rows must lie in one block");
   // Two LDS buffers per tensor: tile n is read from one while tile n+1 is
-  // written to the other.  Separate objects, so the compiler can tell a
-  // pending direct-to-LDS load into one from reads of the other.
-  //  - Fresh prompt (PB = 0): K and V tiles row-major [key][dim], dense
-  //    (2*D bytes per row), filled by buffer loads straight into LDS.  The
-  //    16-byte chunks of each row are XOR-swizzled by the row index, so
-  //    that the fragment reads below touch every bank evenly.
-  //  - Paged (PB > 0): K row-major padded to KROW bytes, V transposed to
-  //    [dim][key] padded to VROW bytes, both staged through registers.
-  constexpr int ROWB = D * 2;                        // bytes of one dense row
-  constexpr int CPR = ROWB / 16;                     // 16-byte chunks per dense row
-  constexpr int KBUF = PAGED ? BN * KROW : BN * ROWB;
-  constexpr int VBUF = PAGED ? D * VROW : BN * ROWB;
-  __shared__ __attribute__((aligned(1024))) unsigned char k_lds0[KBUF], k_lds1[KBUF];
-  __shared__ __attribute__((aligned(1024))) unsigned char v_lds0[VBUF], v_lds1[VBUF];
+  // loaded into the other.  Tiles are row-major [key][dim], dense, filled by
+  // buffer loads that write LDS directly.  The 16-byte chunks of each row are
+  // XOR-swizzled by the row index, so that the fragment reads below touch
+  // every bank evenly.  Separate objects, so the compiler can tell a pending
+  // load into one buffer from the reads of the other.
+  __shared__ __attribute__((aligned(1024))) unsigned char k_lds0[TILE], k_lds1[TILE];
+  __shared__ __attribute__((aligned(1024))) unsigned char v_lds0[TILE], v_lds1[TILE];
   auto kbuf = [&](int b) -> unsigned char* { return b ? k_lds1 : k_lds0; };
   auto vbuf = [&](int b) -> unsigned char* { return b ? v_lds1 : v_lds0; };
-  // Swizzled chunk of a dense row: K's fragment reads take one 16-byte chunk
-  // from each of 16 consecutive rows, V's transposing reads take 8 bytes from
-  // each of 8 consecutive rows in runs of 4 chunks.
-  auto kswz = [](int row, int c) { return D == 128 ? c ^ (row & 15) : c ^ ((row >> 1) & 7); };
-  auto vswz = [](int row, int c) { return D == 128 ? c ^ (4 * (row & 3)) : c ^ (4 * ((row >> 1) & 1)); };
+  // Swizzled chunk of a row: K's fragment reads take one 16-byte chunk from
+  // each of 16 consecutive rows; V's transposing reads take 8 bytes from each
+  // of 8 consecutive rows, in runs of 4 chunks.  Each is an involution.
+  auto kswz = [](int row, int ch) { return D == 128 ? ch ^ (row & 15) : ch ^ ((row >> 1) & 7); };
+  auto vswz = [](int row, int ch) { return D == 128 ? ch ^ (4 * (row & 3)) : ch ^ (4 * ((row >> 1) & 1)); };
 
   // Work item w enumerates (head, prompt, query tile), tile fastest and longest
   // first.  With the XCD remap, each XCD walks a contiguous range of w.  All
@@ -218,9 +207,8 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
   for (int sft = 32; sft >= 1; sft >>= 1) off += __shfl_xor(off, sft, 64);
   // Every lane holds the same sum; make that visible to the compiler, so that
   // the buffer descriptors built from it live in scalar registers.
-  if constexpr (!PAGED)
-    off = (long long)(((unsigned long long)(uint32_t)__builtin_amdgcn_readfirstlane((int)(off >> 32)) << 32) |
-                      (uint32_t)__builtin_amdgcn_readfirstlane((int)off));
+  off = (long long)(((unsigned long long)(uint32_t)__builtin_amdgcn_readfirstlane((int)(off >> 32)) << 32) |
+                    (uint32_t)__builtin_amdgcn_readfirstlane((int)off));
   if (off + L > a.total_tokens) L = (int)max(0ll, (long long)a.total_tokens - off);
   // C: cached prefix tokens ahead of the new ones; keys are indexed by absolute
   // position 0 .. C+L-1, and new token i sits at position C + i.
@@ -257,33 +245,13 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
     for (int kk = 0; kk < KS; ++kk) qf[kk] = make_uint4(0u, 0u, 0u, 0u);
   }
 
-  // Per-thread staging slots (fixed for the whole loop): K chunk i is row
-  // krow[i], chunk kch[i] of the tile; the V group is keys 4*vg..+3, dims vch*8..+7.
-  int krow[KCH], kch[KCH];
-  uint32_t koff[KCH], klds[KCH];
-#pragma unroll
-  for (int i = 0; i < KCH; ++i) {
-    const int idx = threadIdx.x + i * 256;
-    krow[i] = idx / (D / 8);
-    kch[i] = idx % (D / 8);
-    koff[i] = krow[i] * rsb + kch[i] * 16;
-    klds[i] = krow[i] * KROW + kch[i] * 16;
-  }
-  const int vg = threadIdx.x % (BN / 4), vch = threadIdx.x / (BN / 4);
-  const uint32_t voff = 4 * vg * rsb + vch * 16;
-  const uint32_t vlds = (vch * 8) * VROW + vg * 8;
-
-  // Staging registers: the next tile's K chunks and V group, loaded from HBM
-  // while the current tile is being multiplied.
-  struct Stage {
-    uint4 k[KCH];
-    uint4 v[4];
-  };
-  Stage sa;
-  // Block ids of the next tile to be staged (paged form only): lane j of each
-  // wave holds the id of the tile's block j.
+  // Paged form: the block ids of the next tile to be loaded, one tile ahead
+  // (lane j of each wave holds the id of the tile's block j), and the first
+  // key that lies in a block outside the pool.  Such a block is never read;
+  // every query that would see it gets NaN.
   constexpr int NBT = PAGED ? BN / PB : 1;
   int idv = 0;
+  int bad_key = 0x7fffffff;
   auto load_ids = [&](int n0) {
     if constexpr (PAGED) {
       const int e = (n0 >> SH) + lane;
@@ -292,93 +260,39 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
     }
   };
   load_ids(0);
-  auto gload = [&](Stage& st_, int n0) __attribute__((always_inline)) {
-    uint4 (&kst)[KCH] = st_.k;
-    uint4 (&vst)[4] = st_.v;
+
+  // The tile at key n0 straight from HBM into LDS buffer b.  Each wave load
+  // fills one 1 KiB run of RPI rows: lane l's 16 bytes land at byte 16*l of
+  // the run, so it loads the logical chunk that the swizzle puts there.  The
+  // buffer descriptor covers exactly the rows that exist: rows past the end
+  // (and every row of a block outside the pool) read as zeros.
+  auto gdma = [&](int n0, int b) __attribute__((always_inline)) {
     if constexpr (PAGED) {
-      // The tile's NBT block ids were loaded one tile ahead: lane j of every
-      // wave holds block j's id.  Key n0 + r lies in block r >> SH of the
-      // tile, at row r & (PB - 1).  Every load reads inside the pool; an id
-      // outside the pool then yields NaN, so the result shows it, and a key
-      // at or past the end reads as zero.
-      const uint4 nanv = make_uint4(E16_NAN2, E16_NAN2, E16_NAN2, E16_NAN2);
-      const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
-      auto fetch = [&](const char* pool, int r, int ph, int ch) -> uint4 {
-        const bool bad = (uint64_t)(uint32_t)ph >= (uint64_t)a.num_blocks;
-        const int64_t row = (((int64_t)(bad ? 0 : ph) * a.num_heads + h) << SH) + (r & (PB - 1));
-        const uint4 x = *reinterpret_cast<const uint4*>(pool + row * (D * 2) + ch * 16);
-        return n0 + r >= C + L ? zero : bad ? nanv : x;
-      };
+      const unsigned long long badm = __ballot(lane < NBT && (uint64_t)(uint32_t)idv >= (uint64_t)a.num_blocks);
+      if (badm != 0ull) bad_key = min(bad_key, n0 + ((int)__builtin_ctzll(badm) << SH));
       const char* kpool = reinterpret_cast<const char*>(a.k_cache);
       const char* vpool = reinterpret_cast<const char*>(a.v_cache);
 #pragma unroll
-      for (int i = 0; i < KCH; ++i) {
-        // The chunk's block is the same for the whole wave.
-        const int j = __builtin_amdgcn_readfirstlane(krow[i] >> SH);
-        kst[i] = fetch(kpool, krow[i], __builtin_amdgcn_readlane(idv, j), kch[i]);
-      }
-      if (threadIdx.x < VG) {
-        const int ph = __shfl(idv, (4 * vg) >> SH, 64);  // rows 4vg .. 4vg+3 share a block
-#pragma unroll
-        for (int i = 0; i < 4; ++i) vst[i] = fetch(vpool, 4 * vg + i, ph, vch);
+      for (int j = 0; j < IPW; ++j) {
+        const int blk = w * IPW + j;
+        const int row0 = blk * RPI;  // first row of the run, within the tile
+        const int key0 = n0 + row0;
+        const int ph = __builtin_amdgcn_readlane(idv, row0 >> SH);
+        const bool ok = (uint64_t)(uint32_t)ph < (uint64_t)a.num_blocks;
+        const int valid = ok ? min(max(C + L - key0, 0), RPI) : 0;
+        const int64_t first = ((((int64_t)(ok ? ph : 0) * a.num_heads + h) << SH) + (key0 & (PB - 1))) * ROWB;
+        const __amdgpu_buffer_rsrc_t rk =
+            __builtin_amdgcn_make_buffer_rsrc((void*)(kpool + first), (short)0, valid * ROWB, BUF_RSRC_WORD3);
+        const __amdgpu_buffer_rsrc_t rv =
+            __builtin_amdgcn_make_buffer_rsrc((void*)(vpool + first), (short)0, valid * ROWB, BUF_RSRC_WORD3);
+        const int r = lane / CPR, pc = lane % CPR;
+        buffer_load_lds16(rk, kbuf(b) + blk * 1024, r * ROWB + kswz(row0 + r, pc) * 16);
+        buffer_load_lds16(rv, vbuf(b) + blk * 1024, r * ROWB + vswz(row0 + r, pc) * 16);
       }
       load_ids(n0 + BN);
     } else {
-      const char* kt = kb + (int64_t)n0 * rsb;
-      const char* vt = vb + (int64_t)n0 * rsb;
-      // Buffer loads over exactly this tile's rows that exist: a row at or past
-      // the prompt end lies at or beyond num_records, so the hardware returns
-      // zeros for it.  (Row r of the tile starts at r * rsb; the last existing
-      // row ends at (rows - 1) * rsb + 2 * D, and rsb >= 2 * D.)  Offsets stay
-      // below 64 * rsb <= 64 * 65535 * 128 * 2 < 2^31 under the ABI's limits.
-      const int rows = min(L - n0, BN);  // >= 1: n0 < L here
-      const int nrec = (rows - 1) * (int)rsb + D * 2;
-      const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)kt, (short)0, nrec, BUF_RSRC_WORD3);
-      const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)vt, (short)0, nrec, BUF_RSRC_WORD3);
-#pragma unroll
-      for (int i = 0; i < KCH; ++i)
-        kst[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, (int)koff[i], 0, 0));
-      if (threadIdx.x < VG) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          vst[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, (int)(voff + i * rsb), 0, 0));
-      }
-    }
-  };
-  // K row-major [key][dim]; V transposed to [dim][key], 4 keys per 8-byte store.
-  auto lstore = [&](const Stage& st_, int buf) __attribute__((always_inline)) {
-    const uint4 (&kst)[KCH] = st_.k;
-    const uint4 (&vst)[4] = st_.v;
-#pragma unroll
-    for (int i = 0; i < KCH; ++i) *reinterpret_cast<uint4*>(kbuf(buf) + klds[i]) = kst[i];
-    if (threadIdx.x < VG) {
-      const uint32_t w0[4] = {vst[0].x, vst[0].y, vst[0].z, vst[0].w};
-      const uint32_t w1[4] = {vst[1].x, vst[1].y, vst[1].z, vst[1].w};
-      const uint32_t w2[4] = {vst[2].x, vst[2].y, vst[2].z, vst[2].w};
-      const uint32_t w3[4] = {vst[3].x, vst[3].y, vst[3].z, vst[3].w};
-#pragma unroll
-      for (int qd = 0; qd < 4; ++qd) {  // dword qd holds dims vch*8 + 2qd and 2qd+1
-        // v_perm picks 16-bit halves: 0x05040100 = (low of src1, low of src0),
-        // 0x07060302 = (high of src1, high of src0).
-        const uint2 even = make_uint2(__builtin_amdgcn_perm(w1[qd], w0[qd], 0x05040100u),
-                                      __builtin_amdgcn_perm(w3[qd], w2[qd], 0x05040100u));
-        const uint2 odd = make_uint2(__builtin_amdgcn_perm(w1[qd], w0[qd], 0x07060302u),
-                                     __builtin_amdgcn_perm(w3[qd], w2[qd], 0x07060302u));
-        *reinterpret_cast<uint2*>(vbuf(buf) + vlds + (2 * qd) * VROW) = even;
-        *reinterpret_cast<uint2*>(vbuf(buf) + vlds + (2 * qd + 1) * VROW) = odd;
-      }
-    }
-  };
-
-  // Fresh prompt: the tile at key n0 straight from HBM into LDS buffer b.
-  // Each wave instruction fills one 1 KiB run of the dense tile (RPI rows):
-  // lane l lands at byte 16*l of the run, so it loads the logical chunk that
-  // the swizzle puts there.  Rows at or past the prompt end lie at or beyond
-  // num_records and are written as zeros.
-  auto gdma = [&](int n0, int b) __attribute__((always_inline)) {
-    if constexpr (!PAGED) {
-      constexpr int RPI = 1024 / ROWB;   // rows per wave instruction
-      constexpr int IPW = BN / RPI / 4;  // instructions per wave per tensor
+      // Offsets stay below 64 * rsb <= 64 * 65535 * 128 * 2 < 2^31 under the
+      // ABI's limits.
       const int rows = min(L - n0, BN);  // >= 1: n0 < L here
       const int nrec = (rows - 1) * (int)rsb + D * 2;
       const __amdgpu_buffer_rsrc_t rk =
@@ -395,10 +309,11 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
       }
     }
   };
-  // The loads into LDS above complete asynchronously: wait for this wave's
-  // before the barrier that publishes the tile.
-  auto dma_wait = [&]() {
-    if constexpr (!PAGED) wait_vmem();
+  // The loads into LDS complete asynchronously: each wave waits for its own,
+  // then the barrier publishes the tile to the whole workgroup.
+  auto publish = [&]() __attribute__((always_inline)) {
+    wait_vmem();
+    __syncthreads();
   };
 
   f32x16_t o[DB];
@@ -436,8 +351,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const int row = u * 32 + ql;
-        const unsigned char* kr = PAGED ? kbuf(buf) + row * KROW + (2 * kk + hf) * 16
-                                        : kbuf(buf) + row * ROWB + kswz(row, 2 * kk + hf) * 16;
+        const unsigned char* kr = kbuf(buf) + row * ROWB + kswz(row, 2 * kk + hf) * 16;
         st[u] = mfma32<E>(*reinterpret_cast<const uint4*>(kr), qf[kk], st[u]);
       }
 
@@ -476,7 +390,11 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
       }
 
     // O^T += V^T P^T in k-steps of 16 keys.  In step (u, kk2), element i of lane
-    // (ql, hf) stands for key n0 + 32u + 16*kk2 + 8*(i/4) + 4*hf + i%4 on both operands.
+    // (ql, hf) stands for key n0 + 32u + 16*kk2 + 8*(i/4) + 4*hf + i%4 on both
+    // operands.  V^T comes from transposing reads: in each group of 16 lanes,
+    // lane i points at 4 values of row kb0 + i/4, dims d0 + 4*(i%4); lane j
+    // then receives dim d0 + j of rows kb0 .. kb0+3.
+    const int i16 = ql & 15;
 #pragma unroll
     for (int u = 0; u < 2; ++u)
 #pragma unroll
@@ -485,23 +403,12 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
         const int kb0 = u * 32 + 16 * kk2 + 4 * hf;  // key within the LDS tile
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          uint2 lo, hi;
-          if constexpr (PAGED) {
-            const unsigned char* vr = vbuf(buf) + (db * 32 + ql) * VROW;
-            lo = *reinterpret_cast<const uint2*>(vr + kb0 * 2);
-            hi = *reinterpret_cast<const uint2*>(vr + (kb0 + 8) * 2);
-          } else {
-            // Transposing reads (ds_read_b64_tr_b16): in each group of 16
-            // lanes, lane i points at 4 values of row kb0 + i/4, dims
-            // d0 + 4*(i%4); lane j then receives dim d0 + j of rows kb0 .. kb0+3.
-            const int i16 = ql & 15;
-            const int dim = db * 32 + (ql & 16) + 4 * (i16 & 3);
-            auto tr = [&](int row) __attribute__((always_inline)) {
-              return lds_read_tr16(vbuf(buf) + row * ROWB + vswz(row, dim >> 3) * 16 + (dim & 7) * 2);
-            };
-            lo = tr(kb0 + (i16 >> 2));
-            hi = tr(kb0 + 8 + (i16 >> 2));
-          }
+          const int dim = db * 32 + (ql & 16) + 4 * (i16 & 3);
+          auto tr = [&](int row) __attribute__((always_inline)) {
+            return lds_read_tr16(vbuf(buf) + row * ROWB + vswz(row, dim >> 3) * 16 + (dim & 7) * 2);
+          };
+          const uint2 lo = tr(kb0 + (i16 >> 2));
+          const uint2 hi = tr(kb0 + 8 + (i16 >> 2));
           o[db] = mfma32<E>(make_uint4(lo.x, lo.y, hi.x, hi.y), pb, o[db]);
         }
       }
@@ -510,34 +417,20 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
   // Tiles below nfull hold keys that every query of the workgroup sees, all
   // before the prompt end (C + m0 < C + L): no masking.  The remaining tiles
   // (at most three) straddle a diagonal or the prompt end; a wave skips a
-  // tile that lies wholly in its queries' future.
+  // tile that lies wholly in its queries' future.  Tile t+1 is loaded while
+  // tile t is multiplied; one barrier per tile.
   const int ntiles = (kend + BN - 1) / BN;
   const int nfull = min((C + m0) / BN, ntiles);
-  // Stage tile t+1 while tile t is multiplied: through registers (paged) or
-  // straight into LDS (fresh prompt); one barrier per tile.
-  auto stage = [&](int n0, int b) __attribute__((always_inline)) {
-    if constexpr (PAGED) gload(sa, n0);
-    else gdma(n0, b);
-  };
-  auto publish = [&](bool more, int b) __attribute__((always_inline)) {
-    if constexpr (PAGED) {
-      if (more) lstore(sa, b);
-    } else {
-      dma_wait();
-    }
-    __syncthreads();
-  };
-  stage(0, 0);
-  publish(true, 0);
+  gdma(0, 0);
+  publish();
   // Steps are unrolled in pairs, so that every LDS address names its buffer
   // at compile time (the compiler then sees that a load into one buffer and
   // the reads of the other do not overlap).
-  auto step = [&](auto masked_c, auto buf_c, int t) __attribute__((always_inline)) {
+  auto step = [&](auto masked_c, auto buf_c, int tt) __attribute__((always_inline)) {
     constexpr int b = decltype(buf_c)::value;
-    const bool more = t + 1 < ntiles;
-    if (more) stage((t + 1) * BN, b ^ 1);
-    if (!decltype(masked_c)::value || t * BN < wkend) tile(masked_c, b, t * BN);
-    publish(more, b ^ 1);
+    if (tt + 1 < ntiles) gdma((tt + 1) * BN, b ^ 1);
+    if (!decltype(masked_c)::value || tt * BN < wkend) tile(masked_c, b, tt * BN);
+    publish();
   };
   using B0 = std::integral_constant<int, 0>;
   using B1 = std::integral_constant<int, 1>;
@@ -553,7 +446,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
   lrow += __shfl_xor(lrow, 32, 64);  // the two halves' partial row sums
 
   if (qi < L) {
-    const float inv = 1.0f / lrow;
+    const float inv = (PAGED && lim >= bad_key) ? __builtin_nanf("") : 1.0f / lrow;
     const int64_t ob = (off + qi) * rs + (int64_t)h * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db)

@@ -232,3 +232,29 @@ def test_cached_prefix_prefill_block_sizes(bs):
     ref = oracle.attention.prefix_prefill(qn, hk, hv, tables, [C] * len(plens), plens, 1 / math.sqrt(D), dt,
                                           block_size=bs)
     assert np.abs(down(out) - ref).max() <= TOL[dt]
+
+
+@pytest.mark.parametrize("bs,D", [(16, 128), (8, 64)])
+def test_cached_prefix_prefill_bad_id_poisons_later_queries(bs, D):
+    """A table entry outside the pool is never read: every query that would see
+    that block gets NaN, the earlier queries are exact."""
+    print(f"cached-prefix prefill bad id, block size {bs}, D={D}", flush=True)
+    dt, H, nb, C, L = "bf16", 4, 40, 40, 100
+    nblk = -(-(C + L) // bs)
+    rng = np.random.default_rng(7)
+    table = rng.permutation(nb)[:nblk].astype(np.int32)[None, :]
+    kc = W.normal((68, 1), (nb, H, bs, D), dt)
+    vc = W.normal((68, 2), (nb, H, bs, D), dt)
+    qn = W.normal((68, 3), (L, H, D), dt)
+    jb = 96 // bs  # the block holding key position 96
+    bad = table.copy()
+    bad[0, jb] = nb + 5
+    out = torch.empty((L, H, D), dtype=torch.float32, device="cuda")
+    ops.paged_attn_prefill_cached(up(qn, dt), up(kc, dt), up(vc, dt), up(bad), up(np.asarray([C], np.int32)),
+                                  up(np.asarray([L], np.int32)), out, max_prompt_len=L, max_prefix_len=C)
+    got = down(out)
+    first_bad = jb * bs - C  # first query (new-token index) whose keys reach the bad block
+    assert np.isnan(got[first_bad:]).all()
+    ref = oracle.attention.prefix_prefill(qn, kc, vc, table, [C], [L], 1 / math.sqrt(D), dt, block_size=bs)
+    assert np.isfinite(got[:first_bad]).all()
+    assert np.abs(got[:first_bad] - ref[:first_bad]).max() <= TOL[dt]
