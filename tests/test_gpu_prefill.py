@@ -64,7 +64,8 @@ def test_prefill_last_row_matches_decode():
 
 
 def test_mixed_step_config5():
-    """Config 5 at full size: write (8 prompts + 192 decode tokens) -> prefill -> decode + reduce."""
+    """Config 5 at full size: write (8 prompts + 192 decode tokens) -> prefill -> decode + reduce,
+    then the same step with the prefill overlapped with write + decode on a second stream."""
     print("mixed step config 5", flush=True)
     mx = W.mixed_config()
     d, p = mx.decode, mx.prefill
@@ -86,6 +87,21 @@ def test_mixed_step_config5():
                            up(p.prompt_lens), pout, max_prompt_len=int(p.prompt_lens.max()))
     dout = run_decode(ops, t, d, "f32")
     torch.cuda.synchronize()
+
+    # The same step with the prefill on a second stream, concurrent with the
+    # write and the decode (they share no buffer): bit-identical results.
+    side = torch.cuda.Stream()
+    main = torch.cuda.current_stream()
+    pout2 = torch.empty_like(pout)
+    side.wait_stream(main)
+    with torch.cuda.stream(side):
+        ops.paged_attn_prefill(up(p.q, p.dtype), up(p.k, p.dtype), up(p.v, p.dtype), up(p.block_tables),
+                               up(p.prompt_lens), pout2, max_prompt_len=int(p.prompt_lens.max()))
+    ops.kv_cache_write(up(k_all, d.dtype), up(v_all, d.dtype), up(sm), t["k_cache"], t["v_cache"])
+    dout2 = run_decode(ops, t, d, "f32")
+    main.wait_stream(side)
+    torch.cuda.synchronize()
+    assert torch.equal(pout, pout2) and torch.equal(dout, dout2)
 
     ek, ev = oracle.attention.cache_write(d.k_cache, d.v_cache, k_all, v_all, sm, B)
     assert np.array_equal(bits(down(t["k_cache"])), bits(ek))
