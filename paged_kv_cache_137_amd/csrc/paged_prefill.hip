@@ -9,10 +9,10 @@
 // Design for CDNA4 (the pages give no kernel for this step):
 //  - Workgroup = 4 wavefronts = 128 query rows of one (prompt, head).  Each wave
 //    owns 32 queries.  Key/value tiles of 64 rows are staged in LDS and shared.
-//    LDS is double-buffered: the next tile's K/V are loaded from HBM into
-//    registers before the current tile's products, and stored to the other
-//    buffer after them, so HBM latency hides behind the matrix cores.  There is
-//    one barrier per tile.
+//    LDS is double-buffered: the next tile's K/V go from HBM straight into
+//    LDS (buffer loads that write LDS, no registers on the way) while the
+//    current tile is multiplied.  Each wave waits for its own loads, then one
+//    barrier per tile publishes the tile.
 //  - A 64-key tile's two 32-key score chains are issued together, so their
 //    MFMAs interleave.  Each half-wave keeps a lane-local partial row sum
 //    against a shared reference maximum.  The halves exchange only when that
@@ -25,8 +25,8 @@
 //  - The output is accumulated transposed as well: O^T += V^T P^T, so the
 //    per-query rescale stays lane-local.  P^T is fed from the score registers
 //    directly.  Its key order inside an MFMA k-step follows the accumulator
-//    layout.  V^T is read from LDS in that same key order.  V is written into
-//    LDS transposed ([dim][key]) when it is staged.
+//    layout.  V stays row-major in LDS; the V^T operand comes from gfx950's
+//    transposing LDS reads (ds_read_b64_tr_b16) in that same key order.
 //  - Probabilities are exp2(s * scale * log2 e - m): one FMA and one v_exp each.
 //    They are rounded once to the input type for the MFMA.  The row sum adds
 //    the rounded values (v_dot2 against ones), so the normalisation matches
@@ -39,9 +39,10 @@
 //  - Query tiles are dispatched longest-first (descending tile index), to even
 //    out the causal triangle's load.
 //  - Cached-prefix variant: keys and values are gathered from the paged pool
-//    through the prompt's block table.  Each block's run of keys is one
-//    contiguous (block, head) tile.  Positions before the prompt's new tokens are a
-//    shared prefix that is already cached ("vLLM & PagedAttention ...",
+//    through the prompt's block table, with the same LDS tiles: each 1 KiB run
+//    of rows lies in one block, and each wave load gets a buffer descriptor
+//    over exactly that block's rows.  Positions before the prompt's new tokens
+//    are a shared prefix that is already cached ("vLLM & PagedAttention ...",
 //    section VII: the prompt phase runs only over the request's own input).
 //    The causal limit is then shifted by the prefix length.
 #include <type_traits>

@@ -65,6 +65,24 @@ def test_workspace_sizing(lib):
     assert lib.pkv_decode_workspace_bytes(0, 32, 128, 4096, 512) == 0
 
 
+def test_shared_decode_workspace_sizing(lib):
+    # the plain layout with partial results always present, then per-sequence
+    # start tokens (S int32), window records (ceil(S/4) int32), and the group
+    # partials (S x H x P x (D + 2) floats); each region 16-byte aligned
+    a16 = lambda x: (x + 15) & ~15  # noqa: E731
+    S, H, D, P = 256, 32, 128, 8
+    plain = 16 + a16(S * P * 4) + S * H * P * (D + 2) * 4
+    want = a16(plain) + a16(S * 4) + a16((S + 3) // 4 * 4) + S * H * P * (D + 2) * 4
+    assert lib.pkv_decode_shared_workspace_bytes(S, H, D, 4096, 512) == want
+    # one partition: the partials are still there (a group member merges its own
+    # partition with its group's)
+    one = 16 + a16(S * 4) + S * H * (D + 2) * 4
+    assert lib.pkv_decode_shared_workspace_bytes(S, H, D, 512, 512) == (
+        a16(one) + a16(S * 4) + a16(S // 4 * 4) + S * H * (D + 2) * 4)
+    assert lib.pkv_decode_shared_workspace_bytes(0, H, D, 4096, 512) == 0
+    assert lib.pkv_decode_shared_workspace_bytes(S, H, D, 4096, 512) > lib.pkv_decode_workspace_bytes(S, H, D, 4096, 512)
+
+
 def test_bad_arguments_rejected_before_any_launch(lib):
     desc = _lib.CacheDesc(64, 4, 128, 16, _lib.PKV_BF16)
     null = ctypes.c_void_p(0)
@@ -93,6 +111,19 @@ def test_bad_arguments_rejected_before_any_launch(lib):
     # decode: empty batch is a no-op
     rc = lib.pkv_paged_attn_decode(null, null, null, ctypes.byref(desc), null, 4, null, 0, 64, 1.0, null, 0, 512,
                                    null, 0, null)
+    assert rc == _lib.PKV_OK
+    # shared-prefix decode: the same checks as the plain decode
+    rc = lib.pkv_paged_attn_decode_shared(null, null, null, ctypes.byref(desc), null, 4, null, 1, 65, 1.0, null, 0,
+                                          512, null, 0, null)
+    assert rc == _lib.PKV_EINVAL
+    rc = lib.pkv_paged_attn_decode_shared(null, null, null, ctypes.byref(desc), null, 4, null, 1, 64, 1.0, null, 0,
+                                          100, null, 0, null)
+    assert rc == _lib.PKV_EINVAL
+    rc = lib.pkv_paged_attn_decode_shared(null, null, null, None, null, 4, null, 1, 64, 1.0, null, 0, 512, null, 0,
+                                          null)
+    assert rc == _lib.PKV_EINVAL
+    rc = lib.pkv_paged_attn_decode_shared(null, null, null, ctypes.byref(desc), null, 4, null, 0, 64, 1.0, null, 0,
+                                          512, null, 0, null)
     assert rc == _lib.PKV_OK
     # prefill: fp32 inputs are not built; head_dim 96 is not built
     rc = lib.pkv_paged_attn_prefill(null, null, null, 4, 128, _lib.PKV_F32, null, 0, null, 1, 10, 10, 1.0, null, 0,
