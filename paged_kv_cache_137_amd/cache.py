@@ -23,6 +23,14 @@ class PagedKVCache:
         self.v_cache = torch.empty(shape, dtype=dtype, device=device)
 
     @classmethod
+    def pinned_host(cls, num_blocks: int, num_heads: int, head_dim: int, block_size: int = 16,
+                    dtype: torch.dtype = torch.bfloat16) -> "PagedKVCache":
+        """A pool of the same layout in pinned host memory, the target of swap_out."""
+        shape = (num_blocks, num_heads, block_size, head_dim)
+        return cls.from_tensors(torch.empty(shape, dtype=dtype, pin_memory=True),
+                                torch.empty(shape, dtype=dtype, pin_memory=True))
+
+    @classmethod
     def from_tensors(cls, k_cache: torch.Tensor, v_cache: torch.Tensor) -> "PagedKVCache":
         self = cls.__new__(cls)
         self.k_cache, self.v_cache = k_cache, v_cache
@@ -54,3 +62,21 @@ class PagedKVCache:
 
     def paged_attn_decode(self, q, block_tables, context_lens, scale, out, **kw):
         return ops.paged_attn_decode(q, self.k_cache, self.v_cache, block_tables, context_lens, scale, out, **kw)
+
+    def paged_attn_decode_shared(self, q, block_tables, context_lens, scale, out, **kw):
+        """paged_attn_decode that reads blocks shared by neighbouring sequences once."""
+        return ops.paged_attn_decode_shared(q, self.k_cache, self.v_cache, block_tables, context_lens, scale, out,
+                                            **kw)
+
+    def paged_attn_prefill_cached(self, q, block_tables, prefix_lens, prompt_lens, out, **kw):
+        """Prompt phase of new tokens over cached prefixes, everything read through the tables."""
+        return ops.paged_attn_prefill_cached(q, self.k_cache, self.v_cache, block_tables, prefix_lens, prompt_lens,
+                                             out, **kw)
+
+    def swap_out(self, host: "PagedKVCache", block_pairs: torch.Tensor) -> None:
+        """Copy (device block, host block) pairs from this pool into a pinned host pool."""
+        ops.swap_blocks(self.k_cache, self.v_cache, host.k_cache, host.v_cache, block_pairs)
+
+    def swap_in(self, host: "PagedKVCache", block_pairs: torch.Tensor) -> None:
+        """Copy (host block, device block) pairs from a pinned host pool into this pool."""
+        ops.swap_blocks(host.k_cache, host.v_cache, self.k_cache, self.v_cache, block_pairs)
