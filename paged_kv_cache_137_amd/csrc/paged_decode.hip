@@ -100,23 +100,58 @@ __global__ __launch_bounds__(1024) void decode_plan_kernel(const DecodeArgs a) {
   __shared__ int cnt[PLAN_BUCKETS];
   const int BS = a.block_size;
   const int part_tokens = a.part_blocks * BS;
+  const int P = a.num_parts;
   for (int i = threadIdx.x; i < PLAN_BUCKETS; i += blockDim.x) cnt[i] = 0;
   __syncthreads();
-  // Threads walk the (sequence, partition) pairs directly, so that the loads
-  // of different partitions of one sequence are issued in parallel.
-  const int npairs = a.num_seqs * a.num_parts;
-  for (int i = threadIdx.x; i < npairs; i += blockDim.x) {
-    const int s = i / a.num_parts;
-    const int p = i - s * a.num_parts;
+  // Pair i = (sequence i / P, partition i % P) gets a bucket (-1: no entry)
+  // and its work-list entry.  All loads of a pair are independent of one
+  // another except the table reads, which need the partition's first block:
+  // two round trips to memory per batch of pairs.  A partition is tagged
+  // shared (read with cached loads, so that the repeats hit in L2) when a
+  // neighbouring sequence holds the same physical block at its first logical
+  // position; the neighbours' table entries are read unconditionally (they are
+  // in bounds) and used only where the neighbour's context reaches them.
+  const int npairs = a.num_seqs * P;
+  auto classify = [&](int i, int& bucket, int& entry) __attribute__((always_inline)) {
+    bucket = -1;
+    entry = 0;
+    if (i >= npairs) return;
+    const int s = i / P;
+    const int p = i - s * P;
     const int ctx = clamp_ctx(a, s);
-    if (ctx <= 0) {
-      if (p == 0) atomicAdd(&cnt[0], 1);
-      continue;
-    }
+    const int ctx_l = s > 0 ? clamp_ctx(a, s - 1) : 0;
+    const int ctx_r = s + 1 < a.num_seqs ? clamp_ctx(a, s + 1) : 0;
     const int t0 = seq_start(a, s) + p * part_tokens;
-    if (t0 >= ctx) continue;
+    if (ctx <= 0) {
+      // One entry, in the smallest bucket, so that the output is written as NaN.
+      if (p == 0) {
+        bucket = 0;
+        entry = (s * P) << 1;
+      }
+      return;
+    }
+    if (t0 >= ctx) return;
     const int nb = (min(part_tokens, ctx - t0) + BS - 1) / BS;
-    atomicAdd(&cnt[min(nb, PLAN_BUCKETS - 1)], 1);
+    const int lb = t0 / BS;
+    const int32_t* row = a.block_tables + (int64_t)s * a.max_blocks_per_seq + lb;
+    const int mine = row[0];
+    const int left = s > 0 ? row[-a.max_blocks_per_seq] : 0;
+    const int right = s + 1 < a.num_seqs ? row[a.max_blocks_per_seq] : 0;
+    const int shared = (ctx_l > lb * BS && left == mine) || (ctx_r > lb * BS && right == mine);
+    bucket = min(nb, PLAN_BUCKETS - 1);
+    entry = ((s * P + p) << 1) | shared;
+  };
+  // Up to R pairs per thread are classified at once (their loads overlap) and
+  // kept in registers for the placement pass; larger batches classify again.
+  constexpr int R = 4;
+  const int per_pass = R * (int)blockDim.x;
+  int bucket[R], entry[R];
+  for (int base = 0; base < npairs; base += per_pass) {
+#pragma unroll
+    for (int k = 0; k < R; ++k) classify(base + threadIdx.x + k * (int)blockDim.x, bucket[k], entry[k]);
+#pragma unroll
+    for (int k = 0; k < R; ++k)
+      if (bucket[k] >= 0) atomicAdd(&cnt[bucket[k]], 1);
   }
   __syncthreads();
   // Exclusive scan of the bucket counts in descending bucket order: thread i
@@ -147,31 +182,18 @@ __global__ __launch_bounds__(1024) void decode_plan_kernel(const DecodeArgs a) {
     }
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < npairs; i += blockDim.x) {
-    const int s = i / a.num_parts;
-    const int p = i - s * a.num_parts;
-    const int ctx = clamp_ctx(a, s);
-    if (ctx <= 0) {
-      if (p == 0) a.work_list[atomicAdd(&cnt[0], 1)] = (s * a.num_parts) << 1;
-      continue;
-    }
-    const int t0 = seq_start(a, s) + p * part_tokens;
-    if (t0 >= ctx) continue;
-    const int32_t* row = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
-    {
-      const int nb = (min(part_tokens, ctx - t0) + BS - 1) / BS;
-      // Shared blocks (parallel samples, a common prefix) are read by several
-      // sequences close together in time; those partitions are read with
-      // cached loads so that the repeats hit in L2.  The sign of sharing used:
-      // a neighbouring sequence holds the same physical block at the
-      // partition's first logical position.
-      const int lb = t0 / BS;
-      const int mine = row[lb];
-      int shared = 0;
-      for (int s2 = max(s - 1, 0); s2 <= min(s + 1, a.num_seqs - 1); ++s2)
-        if (s2 != s && clamp_ctx(a, s2) > lb * BS && a.block_tables[(int64_t)s2 * a.max_blocks_per_seq + lb] == mine)
-          shared = 1;
-      a.work_list[atomicAdd(&cnt[min(nb, PLAN_BUCKETS - 1)], 1)] = ((s * a.num_parts + p) << 1) | shared;
+  auto place = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int k = 0; k < R; ++k)
+      if (bucket[k] >= 0) a.work_list[atomicAdd(&cnt[bucket[k]], 1)] = entry[k];
+  };
+  if (npairs <= per_pass) {
+    place();  // the single batch is still in registers
+  } else {
+    for (int base = 0; base < npairs; base += per_pass) {
+#pragma unroll
+      for (int k = 0; k < R; ++k) classify(base + threadIdx.x + k * (int)blockDim.x, bucket[k], entry[k]);
+      place();
     }
   }
 }

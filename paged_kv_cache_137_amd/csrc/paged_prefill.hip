@@ -317,6 +317,22 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
     __syncthreads();
   };
 
+  // Lane part of the V^T read addresses (transposing reads below).  Lane
+  // (ql, hf) points at row 4*hf + i16/4 of each 16-key step and dims
+  // 32*db + (ql & 16) + 4*(i16 % 4) .. +4; the row's swizzle depends only on
+  // the row modulo 4 (D = 128) or 8 (D = 64), which adding the step's key
+  // offset (a multiple of 8) keeps.
+  int vlane[DB];
+  {
+    const int i16 = ql & 15;
+    const int vrow = 4 * hf + (i16 >> 2);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const int dim = db * 32 + (ql & 16) + 4 * (i16 & 3);
+      vlane[db] = vrow * ROWB + vswz(vrow, dim >> 3) * 16 + (dim & 7) * 2;
+    }
+  }
+
   f32x16_t o[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db)
@@ -394,22 +410,18 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
     // (ql, hf) stands for key n0 + 32u + 16*kk2 + 8*(i/4) + 4*hf + i%4 on both
     // operands.  V^T comes from transposing reads: in each group of 16 lanes,
     // lane i points at 4 values of row kb0 + i/4, dims d0 + 4*(i%4); lane j
-    // then receives dim d0 + j of rows kb0 .. kb0+3.
-    const int i16 = ql & 15;
+    // then receives dim d0 + j of rows kb0 .. kb0+3.  The lane part of each
+    // address is vlane[db]; the step's key offset is a constant.
 #pragma unroll
     for (int u = 0; u < 2; ++u)
 #pragma unroll
       for (int kk2 = 0; kk2 < 2; ++kk2) {
         const uint4 pb = make_uint4(pk[u][4 * kk2], pk[u][4 * kk2 + 1], pk[u][4 * kk2 + 2], pk[u][4 * kk2 + 3]);
-        const int kb0 = u * 32 + 16 * kk2 + 4 * hf;  // key within the LDS tile
+        const int kofs = (u * 32 + 16 * kk2) * ROWB;  // first key of the step, within the LDS tile
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          const int dim = db * 32 + (ql & 16) + 4 * (i16 & 3);
-          auto tr = [&](int row) __attribute__((always_inline)) {
-            return lds_read_tr16(vbuf(buf) + row * ROWB + vswz(row, dim >> 3) * 16 + (dim & 7) * 2);
-          };
-          const uint2 lo = tr(kb0 + (i16 >> 2));
-          const uint2 hi = tr(kb0 + 8 + (i16 >> 2));
+          const uint2 lo = lds_read_tr16(vbuf(buf) + vlane[db] + kofs);
+          const uint2 hi = lds_read_tr16(vbuf(buf) + vlane[db] + kofs + 8 * ROWB);
           o[db] = mfma32<E>(make_uint4(lo.x, lo.y, hi.x, hi.y), pb, o[db]);
         }
       }
