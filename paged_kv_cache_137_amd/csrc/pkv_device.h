@@ -116,7 +116,7 @@ constexpr int DPP_ROW_HALF_MIRROR = 0x141;
 
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float x) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xf, 0xf, false));
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xf, 0xf, true));
 }
 
 // Sum over aligned groups of N lanes (N in 4, 8, 16, 32, 64); every lane of
