@@ -104,6 +104,23 @@ def test_decode_partition_size_independence(part):
     _check(d, out32, None, list(range(d.num_seqs)))
 
 
+def test_decode_many_partitions_plan_batches():
+    """More (sequence, partition) pairs than the plan kernel classifies in one
+    pass (4 per thread x 1024 threads): 1,200 sequences x 4 partitions of 256
+    tokens.  Every sequence is checked against the oracle, and the shared-prefix
+    form (no sharing here) gives the same bits."""
+    print("decode with 4,800 plan pairs", flush=True)
+    lens = [1 + (37 * i) % 1024 for i in range(1200)]
+    d = _batch(43, "f16", lens, H=4, D=64)
+    t = upload_decode(d)
+    out32 = run_decode(ops, t, d, "f32", partition_size=256)
+    _check(d, out32, None, list(range(d.num_seqs)))
+    shared = torch.empty_like(out32)
+    ops.paged_attn_decode_shared(t["q"], t["k_cache"], t["v_cache"], t["block_tables"], t["context_lens"], d.scale,
+                                 shared, max_context_len=d.max_context_len, partition_size=256)
+    assert torch.equal(shared, out32)
+
+
 def test_decode_is_deterministic_and_stages_compose():
     print("decode determinism", flush=True)
     d = W.decode_config(2)
