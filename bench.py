@@ -29,6 +29,8 @@ The same line also carries:
   cached_prefix_prefill  requests prefilling over one cached shared prefix.
   block_size_sweep  the same decode at 8-, 16- and 32-token blocks (the pool's
                 bytes re-tiled, fresh shuffled tables).
+  hbm_reference a contiguous PyTorch sum and copy over the same K pool: practical
+                ceilings for the decode's HBM rate on the same GPU.
   swap          swap-out/swap-in of 2048 blocks between the device pool and a
                 pinned host pool (pkv_swap_blocks), beside a plain contiguous
                 device<->host copy of the same bytes.
@@ -226,6 +228,7 @@ def main() -> int:
     if not a.no_extras:
         line["block_size_sweep"] = block_size_sweep(a, t, d)
         line["swap"] = swap_step(a, t)
+        line["hbm_reference"] = hbm_reference(t)
     del t, ws, out
     torch.cuda.empty_cache()
 
@@ -451,6 +454,36 @@ def cached_prefix_prefill(a, dev, up):
         "TFLOPs": round(flops / (ms * 1e-3) / 1e12, 1),
         "mfma_frac": round(flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
     }
+
+
+def hbm_reference(t):
+    """Plain PyTorch passes over the same K pool on the same GPU, as practical
+    ceilings for the decode's HBM rate: a contiguous sum (read only, fp32
+    accumulation) and a device-to-device copy (read + write).  Timed with HIP
+    events, 20 passes each after 3 warm-up passes."""
+    import torch
+    kc = t["kc"]
+    nbytes = kc.numel() * kc.element_size()
+    dst = torch.empty_like(kc)
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(20):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / 20
+
+    ms_sum = timed(lambda: kc.sum(dtype=torch.float32))
+    ms_copy = timed(lambda: dst.copy_(kc))
+    del dst
+    return {"bytes": nbytes,
+            "torch_sum_ms": round(ms_sum, 4), "torch_sum_read_GBps": round(nbytes / ms_sum / 1e6, 1),
+            "torch_copy_ms": round(ms_copy, 4), "torch_copy_read_plus_write_GBps": round(2 * nbytes / ms_copy / 1e6, 1)}
 
 
 def block_size_sweep(a, t, d):
