@@ -61,7 +61,8 @@ namespace pkv {
 #define PKV_DEC_PP 1
 #endif
 
-constexpr int NW = PKV_DEC_NW;     // wavefronts per workgroup
+constexpr int NW = PKV_DEC_NW;     // wavefronts per workgroup of the per-sequence decode
+constexpr int SNW = 8;             // wavefronts per workgroup of the shared-prefix decode
 constexpr int PLAN_BUCKETS = 257;  // partition sizes 0..256 blocks (larger ones share the top bucket)
 
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
@@ -623,15 +624,15 @@ __device__ __forceinline__ void group_unit(const DecodeArgs& a, int e, int h) {
 }
 
 // Persistent kernel of the shared-prefix form: the group units (window,
-// partition of the shared blocks, NW heads) first, then the per-sequence
+// partition of the shared blocks, SNW heads) first, then the per-sequence
 // units of the plan's list, claimed from one counter, so that the two kinds
 // fill each other's gaps.
 template <typename E, typename O, int D, int BS>
-__global__ __launch_bounds__(NW * 64) void decode_shared_kernel(const DecodeArgs a) {
+__global__ __launch_bounds__(SNW * 64) void decode_shared_kernel(const DecodeArgs a) {
   __shared__ int sm_unit[2];
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int H = a.num_heads;
-  const int HG = (H + NW - 1) / NW;
+  const int HG = (H + SNW - 1) / SNW;
   const int ng = a.num_windows * a.num_parts * HG;
   const int total = ng + a.work_ctrl[1] * HG;
   for (int it = 0;; ++it) {
@@ -642,7 +643,7 @@ __global__ __launch_bounds__(NW * 64) void decode_shared_kernel(const DecodeArgs
     const bool grp = u < ng;
     if (!grp) u -= ng;
     const int e = u / HG;
-    const int h = (u - e * HG) * NW + w;
+    const int h = (u - e * HG) * SNW + w;
     if (h >= H) continue;  // a partial last head group
     if (grp) group_unit<E, O, D, BS>(a, e, h);
     else private_unit<E, O, D, BS>(a, e, h);
@@ -763,11 +764,13 @@ template <typename E, typename O, int D, int BS>
 static hipError_t shared_bs(const DecodeArgs& a, hipStream_t st) {
   hipLaunchKernelGGL(share_detect_kernel, dim3((a.num_windows + 15) / 16), dim3(1024), 0, st, a);
   hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(1024), 0, st, a);
-  const int64_t units = ((int64_t)a.num_windows * a.num_parts + a.total_units) * ((a.num_heads + NW - 1) / NW);
-  // At the kernel's full occupancy: the group units' arithmetic (four
-  // queries per tile) wants the waves that the per-sequence stream does not.
-  const int grid = persistent_grid<decode_shared_kernel<E, O, D, BS>>(NW * 64, units, 64);
-  hipLaunchKernelGGL((decode_shared_kernel<E, O, D, BS>), dim3(grid), dim3(NW * 64), 0, st, a);
+  const int64_t units = ((int64_t)a.num_windows * a.num_parts + a.total_units) * ((a.num_heads + SNW - 1) / SNW);
+  // One 8-wave workgroup per CU (two waves per SIMD): a unit covers 8 heads,
+  // and the group units' arithmetic (four queries per tile) gets a second wave
+  // per SIMD.  Measured faster than 4-wave workgroups at one, two or four per
+  // CU.
+  const int grid = persistent_grid<decode_shared_kernel<E, O, D, BS>>(SNW * 64, units, 1);
+  hipLaunchKernelGGL((decode_shared_kernel<E, O, D, BS>), dim3(grid), dim3(SNW * 64), 0, st, a);
   return hipGetLastError();
 }
 
