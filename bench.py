@@ -23,6 +23,7 @@ The same line also carries:
                 sequences decode), per kernel, with prefill's MFMA rate; and
                 the same step with the prefill on a second stream beside the
                 write and the decode.
+  opt13b_decode the OPT-13B-shape decode step (fp16, 64 sequences, 40 heads).
   sharing_step  parallel sampling over shared prompt blocks: the batched
                 copy-on-write copy, then decode (logical and unique KV GB/s),
                 plain and with the shared-prefix decode.
@@ -238,6 +239,7 @@ def main() -> int:
 
     # ---------------- sharing, copy-on-write and cached-prefix prefill ----------------
     if not a.no_extras:
+        line["opt13b_decode"] = opt13b_decode(a, dev, up)
         line["sharing_step"] = sharing_step(a, dev, up)
         line["cached_prefix_prefill"] = cached_prefix_prefill(a, dev, up)
 
@@ -358,6 +360,29 @@ def _time_events(fn, warmup, steps):
     e1.record()
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / steps
+
+
+def opt13b_decode(a, dev, up):
+    """OPT-13B-shape decode step (fp16, 40 heads x 128, 64 sequences, context
+    lengths U[1, 2048], shuffled blocks): plan + persistent decode + reduce,
+    timed with HIP events."""
+    import torch
+
+    from paged_kv_cache_137_amd import ops
+    from paged_kv_cache_137_amd import workloads as W
+
+    d = W.decode_config(2, poison=False)
+    S, H, D = d.q.shape
+    t = dict(q=up(d.q), kc=up(d.k_cache), vc=up(d.v_cache), bt=up(d.block_tables), cl=up(d.context_lens))
+    out = torch.empty((S, H, D), dtype=torch.float16, device=dev)
+    ws = torch.empty(ops.decode_workspace_bytes(S, H, D, d.max_context_len, 512), dtype=torch.uint8, device=dev)
+    ms = _time_events(lambda: ops.paged_attn_decode(t["q"], t["kc"], t["vc"], t["bt"], t["cl"], d.scale, out,
+                                                    max_context_len=d.max_context_len, partition_size=512,
+                                                    workspace=ws), a.warmup, a.steps)
+    nbytes = int(d.context_lens.sum()) * 2 * H * D * 2
+    return {"workload": "OPT-13B-shape decode step: 64 seqs, 40 heads x 128, fp16, ctx U[1, 2048], shuffled blocks",
+            "sum_context_len": int(d.context_lens.sum()), "ms": round(ms, 4),
+            "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1), "frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
 def sharing_step(a, dev, up):
