@@ -30,6 +30,7 @@ The same line also carries:
   cached_prefix_prefill  requests prefilling over one cached shared prefix.
   block_size_sweep  the same decode at 8-, 16- and 32-token blocks (the pool's
                 bytes re-tiled, fresh shuffled tables).
+  decode_launch_shape  the headline decode at 1, 2 and 4 workgroups per CU.
   hbm_reference a contiguous PyTorch sum and copy over the same K pool: practical
                 ceilings for the decode's HBM rate on the same GPU.
   swap          swap-out/swap-in of 2048 blocks between the device pool and a
@@ -230,6 +231,7 @@ def main() -> int:
         line["block_size_sweep"] = block_size_sweep(a, t, d)
         line["swap"] = swap_step(a, t)
         line["hbm_reference"] = hbm_reference(t)
+        line["decode_launch_shape"] = decode_launch_shape(a, t, d, dargs, dkw)
     del t, ws, out
     torch.cuda.empty_cache()
 
@@ -479,6 +481,33 @@ def cached_prefix_prefill(a, dev, up):
         "TFLOPs": round(flops / (ms * 1e-3) / 1e12, 1),
         "mfma_frac": round(flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
     }
+
+
+def decode_launch_shape(a, t, d, dargs, dkw):
+    """The headline decode (plan + persistent kernel + reduce) with 1, 2 and 4
+    workgroups per CU (the library's default is 1; PKV_DECODE_WG_PER_CU
+    overrides it), timed with HIP events."""
+    from paged_kv_cache_137_amd import ops
+
+    kv_bytes = int(d.context_lens.sum()) * 2 * d.num_heads * d.head_dim * 2
+    old = os.environ.get("PKV_DECODE_WG_PER_CU")
+    res = {}
+    try:
+        for n in (1, 2, 4):
+            os.environ["PKV_DECODE_WG_PER_CU"] = str(n)
+
+            def run():
+                ops.paged_attn_decode_partial(*dargs, **dkw)
+                ops.paged_attn_decode_reduce(*dargs, **dkw)
+
+            ms = _time_events(run, a.warmup, a.steps)
+            res[str(n)] = {"ms": round(ms, 4), "GBps": round(kv_bytes / (ms * 1e-3) / 1e9, 1)}
+    finally:
+        if old is None:
+            os.environ.pop("PKV_DECODE_WG_PER_CU", None)
+        else:
+            os.environ["PKV_DECODE_WG_PER_CU"] = old
+    return {"workgroups_per_cu": res}
 
 
 def hbm_reference(t):

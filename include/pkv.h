@@ -33,6 +33,9 @@
  *    range, context lengths in [1, max_context_len], slots unique and in range.
  *    This mode synchronises the stream; it is for tests.  A failed check
  *    returns PKV_EINVAL.
+ *  - PKV_DECODE_WG_PER_CU (1 to 16, default 1) sets how many workgroups per CU
+ *    the per-sequence decode keeps resident; it is read at every launch and
+ *    exists to measure other launch shapes.  Results do not depend on it.
  *
  * KV pool layout (both k_cache and v_cache)
  * -----------------------------------------

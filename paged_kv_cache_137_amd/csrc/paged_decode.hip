@@ -44,6 +44,7 @@
 //    them), so two tiles per wave are in flight.
 //  - Masking of slots at or past the context length is a select (-inf score,
 //    zeroed V), never a multiply, so stale NaN data in those slots cannot leak.
+#include <cstdlib>
 #include <type_traits>
 
 #include "pkv_device.h"
@@ -686,23 +687,35 @@ __global__ __launch_bounds__(D) void decode_reduce_shared_kernel(const DecodeArg
 }
 
 // Workgroups of a persistent kernel: per_cu on every CU of the device (at
-// most the kernel's occupancy), never more than there are units.  Cached per
-// kernel and device.
+// most the kernel's occupancy), never more than there are units.  The CU
+// count and the occupancy are cached per kernel and device.
 template <auto KERNEL>
 static int persistent_grid(int block, int64_t units, int per_cu) {
   constexpr int kMaxDev = 64;
-  static int slots[kMaxDev];
+  static int cus_occ[kMaxDev][2];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
-  int n = dev < kMaxDev ? slots[dev] : 0;
-  if (n == 0) {
-    int cus = 0, occ = 0;
+  int cus = dev < kMaxDev ? cus_occ[dev][0] : 0, occ = dev < kMaxDev ? cus_occ[dev][1] : 0;
+  if (cus == 0) {
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, KERNEL, block, 0) != hipSuccess || occ <= 0) occ = 1;
-    n = cus * (occ < per_cu ? occ : per_cu);
-    if (dev < kMaxDev) slots[dev] = n;
+    if (dev < kMaxDev) {
+      cus_occ[dev][0] = cus;
+      cus_occ[dev][1] = occ;
+    }
   }
+  const int64_t n = (int64_t)cus * (occ < per_cu ? occ : per_cu);
   return (int)(units < n ? units : n);
+}
+
+// Workgroups per CU of the per-sequence decode: 1, or the value of the
+// environment variable PKV_DECODE_WG_PER_CU (1 to 16; read at every launch,
+// for measuring other launch shapes).
+static int decode_wg_per_cu() {
+  const char* e = std::getenv("PKV_DECODE_WG_PER_CU");
+  if (e == nullptr) return 1;
+  const int v = std::atoi(e);
+  return v >= 1 && v <= 16 ? v : 1;
 }
 
 template <typename E, typename O, int D, int BS>
@@ -713,7 +726,8 @@ static hipError_t partial_bs(const DecodeArgs& a, hipStream_t st) {
   // kernel at its full occupancy (measured 4% faster on the Llama-2-7B-shape
   // step and 11% on the OPT-13B-shape one): more outstanding requests lower
   // the HBM rate of this random 4 KiB-tile stream instead of raising it.
-  const int grid = persistent_grid<decode_partial_kernel<E, O, D, BS>>(NW * 64, ((int64_t)a.total_units + NW - 1) / NW, 1);
+  const int grid = persistent_grid<decode_partial_kernel<E, O, D, BS>>(NW * 64, ((int64_t)a.total_units + NW - 1) / NW,
+                                                                       decode_wg_per_cu());
   hipLaunchKernelGGL((decode_partial_kernel<E, O, D, BS>), dim3(grid), dim3(NW * 64), 0, st, a);
   return hipGetLastError();
 }

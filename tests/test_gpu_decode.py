@@ -121,6 +121,19 @@ def test_decode_many_partitions_plan_batches():
     assert torch.equal(shared, out32)
 
 
+def test_decode_launch_shape_does_not_change_results(monkeypatch):
+    """The persistent decode gives the same bits at 1, 2 and 4 workgroups per
+    CU (PKV_DECODE_WG_PER_CU): no output depends on which workgroup ran a unit."""
+    print("decode launch shapes", flush=True)
+    d = W.decode_config(2)
+    t = upload_decode(d)
+    outs = []
+    for n in ("1", "2", "4"):
+        monkeypatch.setenv("PKV_DECODE_WG_PER_CU", n)
+        outs.append(run_decode(ops, t, d, "f32"))
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
+
+
 def test_decode_is_deterministic_and_stages_compose():
     print("decode determinism", flush=True)
     d = W.decode_config(2)
