@@ -180,10 +180,16 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
   auto kswz = [](int row, int ch) { return D == 128 ? ch ^ (row & 15) : ch ^ ((row >> 1) & 7); };
   auto vswz = [](int row, int ch) { return D == 128 ? ch ^ (4 * (row & 3)) : ch ^ (4 * ((row >> 1) & 1)); };
 
-  // Work item w enumerates (head, prompt, query tile), tile fastest and longest
-  // first.  With the XCD remap, each XCD walks a contiguous range of w.  All
-  // query tiles of a (prompt, head) then share one XCD's L2, which holds the
-  // K/V they all reread.
+  // Work item wi enumerates (head, item of that head); with the XCD remap each
+  // XCD walks a contiguous range of wi, so all query tiles of a (prompt, head)
+  // share one XCD's L2, which holds the K/V they all reread.
+  //  - Up to PREFILL_DENSE_PROMPTS prompts: a head's items are the query tiles
+  //    that exist, prompt after prompt in order of context length (prefix +
+  //    new tokens), longest first, ties by index, and each prompt's tiles
+  //    longest first.  The long causal rows start first, the short ones fill
+  //    the end, and no workgroup is spent on a tile past a prompt's end.  Each
+  //    workgroup ranks the prompts itself (one per lane).
+  //  - More prompts: every prompt gets num_qtiles items, in index order.
   const int wg = blockIdx.x;
 #if PKV_PRE_XCD
   const int wi = (wg & 7) * a.per_xcd + (wg >> 3);
@@ -191,19 +197,40 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
   const int wi = wg;
 #endif
   if (wi >= a.total_items) return;
-  const int t = wi % a.num_qtiles;
-  const int rest = wi / a.num_qtiles;
-  const int pr = rest % a.num_prompts;
-  const int h = rest / a.num_prompts;
-  const int qt = a.num_qtiles - 1 - t;
-  const int m0 = qt * BM;
-  int L = a.prompt_lens[pr];
-  if (L <= m0) return;
-
-  // Row offset of this prompt: the sum of the earlier prompts' lengths.
+  const int h = wi / a.items_per_head;
+  const int item = wi - h * a.items_per_head;
   const int lane = threadIdx.x & 63;
-  long long off = 0;
-  for (int i = lane; i < pr; i += 64) off += max(a.prompt_lens[i], 0);
+  int pr, qt, L;
+  long long off = 0;  // row offset of the prompt: the sum of the earlier prompts' lengths
+  if (a.num_prompts <= PREFILL_DENSE_PROMPTS) {
+    const int np = a.num_prompts;
+    const int lj = lane < np ? max(a.prompt_lens[lane], 0) : 0;
+    int key = lj;
+    if constexpr (PAGED) {
+      if (a.prefix_lens != nullptr && lane < np) key += max(a.prefix_lens[lane], 0);
+    }
+    const int nq = (int)(((int64_t)lj + BM - 1) / BM);  // this lane's prompt's query tiles
+    // start: tiles of the prompts ahead of this lane's in the order.
+    int start = 0;
+    for (int i = 0; i < np; ++i) {
+      const int ki = __builtin_amdgcn_readlane(key, i);
+      const int ni = __builtin_amdgcn_readlane(nq, i);
+      start += (ki > key || (ki == key && i < lane)) ? ni : 0;
+    }
+    const unsigned long long hit = __ballot(lane < np && item >= start && item < start + nq);
+    if (hit == 0ull) return;  // past the last tile of this head
+    pr = (int)__builtin_ctzll(hit);
+    L = __builtin_amdgcn_readlane(lj, pr);
+    qt = __builtin_amdgcn_readlane(nq, pr) - 1 - (item - __builtin_amdgcn_readlane(start, pr));
+    off = lane < pr ? lj : 0;
+  } else {
+    pr = item / a.num_qtiles;
+    qt = a.num_qtiles - 1 - (item - pr * a.num_qtiles);
+    L = a.prompt_lens[pr];
+    if (L <= qt * BM) return;
+    for (int i = lane; i < pr; i += 64) off += max(a.prompt_lens[i], 0);
+  }
+  const int m0 = qt * BM;
 #pragma unroll
   for (int sft = 32; sft >= 1; sft >>= 1) off += __shfl_xor(off, sft, 64);
   // Every lane holds the same sum; make that visible to the compiler, so that

@@ -328,7 +328,8 @@ int pkv_paged_attn_prefill(const void* q, const void* k, const void* v, int32_t 
       max_blocks_per_seq <= 0)
     return PKV_EINVAL;
   const int32_t num_qtiles = (max_prompt_len + pkv::PREFILL_BLOCK_M - 1) / pkv::PREFILL_BLOCK_M;
-  const int64_t items = (int64_t)num_qtiles * num_heads * num_prompts;
+  const int64_t per_head = pkv::prefill_items_per_head(num_prompts, num_qtiles, total_tokens);
+  const int64_t items = per_head * num_heads;
   if (items > ((int64_t)1 << 31) - 64) return PKV_EINVAL;
   int st = device_status();
   if (st != PKV_OK) return st;
@@ -354,6 +355,7 @@ int pkv_paged_attn_prefill(const void* q, const void* k, const void* v, int32_t 
   a.num_heads = num_heads;
   a.max_prompt_len = max_prompt_len;
   a.num_qtiles = num_qtiles;
+  a.items_per_head = (int32_t)per_head;
   a.total_items = (int32_t)items;
   a.per_xcd = (int32_t)((items + 7) / 8);
   a.scale_log2 = scale * 1.4426950408889634f;
@@ -381,7 +383,8 @@ int pkv_paged_attn_prefill_cached(const void* q, const void* k_cache, const void
       (int64_t)max_blocks_per_seq * desc->block_size < (int64_t)max_prompt_len + (int64_t)max_prefix_len)
     return PKV_EINVAL;
   const int32_t num_qtiles = (max_prompt_len + pkv::PREFILL_BLOCK_M - 1) / pkv::PREFILL_BLOCK_M;
-  const int64_t items = (int64_t)num_qtiles * desc->num_heads * num_prompts;
+  const int64_t per_head = pkv::prefill_items_per_head(num_prompts, num_qtiles, total_tokens);
+  const int64_t items = per_head * desc->num_heads;
   if (items > ((int64_t)1 << 31) - 64) return PKV_EINVAL;
   st = device_status();
   if (st != PKV_OK) return st;
@@ -419,6 +422,7 @@ int pkv_paged_attn_prefill_cached(const void* q, const void* k_cache, const void
   a.num_heads = desc->num_heads;
   a.max_prompt_len = max_prompt_len;
   a.num_qtiles = num_qtiles;
+  a.items_per_head = (int32_t)per_head;
   a.total_items = (int32_t)items;
   a.per_xcd = (int32_t)((items + 7) / 8);
   a.scale_log2 = scale * 1.4426950408889634f;
