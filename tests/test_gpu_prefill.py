@@ -45,6 +45,24 @@ def test_prefill_parity_ragged(dt, D):
             assert np.array_equal(out32[o].astype(np.float64), oracle.attention.to_f64(p.v[o], dt))
 
 
+@pytest.mark.parametrize("n", [63, 64, 65])
+def test_prefill_many_prompts_dense_and_sparse_enumeration(n):
+    """Up to 64 prompts the kernel enumerates only existing query tiles, ranked
+    by length (ties by index); above that every prompt gets the longest
+    prompt's tile count.  Both sides of the boundary, with empty prompts, equal
+    lengths and tile-multiple lengths, against the oracle."""
+    rng = np.random.default_rng(80 + n)
+    lens = [int(rng.choice([0, 1, 128, 129, 130, 255, 256])) if i % 3 else int(rng.integers(1, 400)) for i in range(n)]
+    print(f"prefill {n} prompts, total {sum(lens)}", flush=True)
+    p = W.make_prefill(81, "bf16", 2, 64, lens)
+    out32 = down(_prefill(p))
+    ref = oracle.attention.causal_prefill(p.q, p.k, p.v, p.prompt_lens, 1 / math.sqrt(64), "bf16")
+    assert np.isfinite(out32).all()
+    err = float(np.abs(out32 - ref).max())
+    print(f"  max|err|={err:.3e}", flush=True)
+    assert err <= TOL["bf16"]
+
+
 def test_prefill_last_row_matches_decode():
     print("prefill <-> decode consistency", flush=True)
     dt, H, D, L = "bf16", 4, 128, 777
