@@ -36,8 +36,10 @@
 //  - Causality: key tiles past the workgroup's last query are never loaded.
 //    Key tiles past a wave's last query are skipped by that wave.  Tiles that
 //    straddle the diagonal or the prompt end are masked by selecting -inf.
-//  - Query tiles are dispatched longest-first (descending tile index), to even
-//    out the causal triangle's load.
+//  - Query tiles are dispatched longest first, to even out the causal
+//    triangle's load: prompts in order of context length (up to 64 prompts,
+//    ranked by each workgroup), and each prompt's tiles in descending order.
+//    Only tiles that exist get a workgroup.
 //  - Cached-prefix variant: keys and values are gathered from the paged pool
 //    through the prompt's block table, with the same LDS tiles: each 1 KiB run
 //    of rows lies in one block, and each wave load gets a buffer descriptor
