@@ -247,7 +247,10 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
   if constexpr (PAGED) {
     const int cap = a.max_blocks_per_seq << SH;
     C = a.prefix_lens != nullptr ? min(max(a.prefix_lens[pr], 0), cap) : 0;
-    L = min(L, cap - C);
+    // One value for the whole workgroup: say so, so that the buffer
+    // descriptors built from it stay scalar.
+    C = __builtin_amdgcn_readfirstlane(C);
+    L = __builtin_amdgcn_readfirstlane(min(L, cap - C));
     trow = a.block_tables + (int64_t)pr * a.max_blocks_per_seq;
   }
   if (L <= m0) return;
@@ -309,7 +312,9 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
         const int key0 = n0 + row0;
         const int ph = __builtin_amdgcn_readlane(idv, row0 >> SH);
         const bool ok = (uint64_t)(uint32_t)ph < (uint64_t)a.num_blocks;
-        const int valid = ok ? min(max(C + L - key0, 0), RPI) : 0;
+        // Uniform, but computed through a 64-bit vector compare: say so, or the
+        // compiler wraps each load in a loop over distinct descriptors.
+        const int valid = __builtin_amdgcn_readfirstlane(ok ? min(max(C + L - key0, 0), RPI) : 0);
         const int64_t first = ((((int64_t)(ok ? ph : 0) * a.num_heads + h) << SH) + (key0 & (PB - 1))) * ROWB;
         const __amdgpu_buffer_rsrc_t rk =
             __builtin_amdgcn_make_buffer_rsrc((void*)(kpool + first), (short)0, valid * ROWB, BUF_RSRC_WORD3);
