@@ -233,6 +233,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
     for (int i = lane; i < pr; i += 64) off += max(a.prompt_lens[i], 0);
   }
   const int m0 = qt * BM;
+  L = __builtin_amdgcn_readfirstlane(L);  // one value for the workgroup (keeps descriptors scalar)
 #pragma unroll
   for (int sft = 32; sft >= 1; sft >>= 1) off += __shfl_xor(off, sft, 64);
   // Every lane holds the same sum; make that visible to the compiler, so that
