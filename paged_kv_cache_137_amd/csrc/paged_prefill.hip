@@ -8,15 +8,17 @@
 //
 // Design for CDNA4 (the pages give no kernel for this step):
 //  - Workgroup = 4 wavefronts = 128 query rows of one (prompt, head).  Each wave
-//    owns 32 queries.  Key/value tiles of 64 rows are staged in LDS and shared.
-//    LDS is double-buffered: the next tile's K/V go from HBM straight into
+//    owns 32 queries.  Key/value tiles of 32 rows are staged in LDS and shared
+//    (32 KiB of LDS per workgroup at 128 dims), and three workgroups share a CU:
+//    the third wave per SIMD hides more latency than the larger tiles of two
+//    workgroups saved in barriers.  LDS is double-buffered: the next tile's
+//    K/V go from HBM straight into
 //    LDS (buffer loads that write LDS, no registers on the way) while the
 //    current tile is multiplied.  Each wave waits for its own loads, then one
 //    barrier per tile publishes the tile.
-//  - A 64-key tile's two 32-key score chains are issued together, so their
-//    MFMAs interleave.  Each half-wave keeps a lane-local partial row sum
-//    against a shared reference maximum.  The halves exchange only when that
-//    reference moves (rarely), and once at the end.
+//  - Each half-wave keeps a lane-local partial row sum against a shared
+//    reference maximum.  The halves exchange only when that reference moves
+//    (rarely), and once at the end.
 //  - Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16 on
 //    16-bit inputs and fp32 accumulation.  Each lane's 16 accumulator values
 //    then belong to a single query (its column).  The online softmax (running
@@ -150,12 +152,13 @@ template <> struct Store4<f16_t> {
 //                 positions are a cached prefix; the prompt's new tokens follow
 //                 (their K/V already written).
 template <typename E, typename O, int D, int PB>
-__global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
+__global__ __launch_bounds__(256, 3) void prefill_kernel(const PrefillArgs a) {
   constexpr bool PAGED = PB != 0;
   constexpr int SH = PB == 8 ? 3 : PB == 16 ? 4 : PB == 32 ? 5 : 0;  // log2 of the block size
   static_assert(!PAGED || (1 << SH) == PB, "block size 8, 16 or 32");
   constexpr int BM = PREFILL_BLOCK_M;  // query rows per workgroup (4 waves x 32)
-  constexpr int BN = 64;               // keys per LDS tile
+  constexpr int BN = 32;               // keys per LDS tile
+  constexpr int U = BN / 32;           // 32-key sub-tiles per tile
   constexpr int KS = D / 16;           // k-steps of Q K^T
   constexpr int DB = D / 32;           // 32-row blocks of O^T
   constexpr int ROWB = D * 2;          // bytes of one K or V row
@@ -379,9 +382,9 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
   const int kend = C + min(L, m0 + BM);     // keys any query of the workgroup sees
   const int wkend = C + min(L, qrow0 + 32); // keys any query of this wave sees
 
-  // One 64-key tile from LDS buffer `buf`, starting at key n0, as two
-  // sub-tiles of 32 keys whose score chains are independent, so their MFMAs
-  // interleave.  Lane (ql, hf) score element j of sub-tile u is key
+  // One tile of BN keys from LDS buffer `buf`, starting at key n0, as U
+  // sub-tiles of 32 keys whose score chains are independent (with U > 1 their
+  // MFMAs interleave).  Lane (ql, hf) score element j of sub-tile u is key
   // n0 + 32u + 8*(j/4) + 4*hf + j%4 against query qi.  MASKED tiles select
   // -inf for every key past the query (or past the prompt end).  Every tile
   // body is one instantiation per MASKED value, so the accumulators stay in
@@ -393,15 +396,15 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
   // more than the slack.
   auto tile = [&](auto masked_c, int buf, int n0) __attribute__((always_inline)) {
     constexpr bool MASKED = decltype(masked_c)::value;
-    f32x16_t st[2];
+    f32x16_t st[U];
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
+    for (int u = 0; u < U; ++u)
 #pragma unroll
       for (int j = 0; j < 16; ++j) st[u][j] = 0.f;
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk)
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
+      for (int u = 0; u < U; ++u) {
         const int row = u * 32 + ql;
         const unsigned char* kr = kbuf(buf) + row * ROWB + kswz(row, 2 * kk + hf) * 16;
         st[u] = mfma32<E>(*reinterpret_cast<const uint4*>(kr), qf[kk], st[u]);
@@ -409,7 +412,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
 
     if constexpr (MASKED) {
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
+      for (int u = 0; u < U; ++u) {
         const int room = lim - (n0 + 32 * u + 4 * hf);  // element j is visible iff its offset <= room
 #pragma unroll
         for (int j = 0; j < 16; ++j) st[u][j] = (8 * (j >> 2) + (j & 3) > room) ? -INFINITY : st[u][j];
@@ -417,7 +420,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
     }
     float lmax = st[0][0];
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
+    for (int u = 0; u < U; ++u)
 #pragma unroll
       for (int j = 0; j < 16; ++j) lmax = fmaxf(lmax, st[u][j]);
     const float mt = lmax * c;  // this half's maximum over the tile, log2 units
@@ -432,9 +435,9 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
       mrow = mnew;
     }
 
-    uint32_t pk[2][8];
+    uint32_t pk[U][8];
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
+    for (int u = 0; u < U; ++u)
 #pragma unroll
       for (int jj = 0; jj < 8; ++jj) {
         pk[u][jj] = pack2<E>(fast_exp2(fmaf(st[u][2 * jj], c, -mrow)), fast_exp2(fmaf(st[u][2 * jj + 1], c, -mrow)));
@@ -448,7 +451,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
     // then receives dim d0 + j of rows kb0 .. kb0+3.  The lane part of each
     // address is vlane[db]; the step's key offset is a constant.
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
+    for (int u = 0; u < U; ++u)
 #pragma unroll
       for (int kk2 = 0; kk2 < 2; ++kk2) {
         const uint4 pb = make_uint4(pk[u][4 * kk2], pk[u][4 * kk2 + 1], pk[u][4 * kk2 + 2], pk[u][4 * kk2 + 3]);
@@ -464,7 +467,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
 
   // Tiles below nfull hold keys that every query of the workgroup sees, all
   // before the prompt end (C + m0 < C + L): no masking.  The remaining tiles
-  // (at most three) straddle a diagonal or the prompt end; a wave skips a
+  // (at most BM / BN + 1) straddle a diagonal or the prompt end; a wave skips a
   // tile that lies wholly in its queries' future.  Tile t+1 is loaded while
   // tile t is multiplied; one barrier per tile.
   const int ntiles = (kend + BN - 1) / BN;
