@@ -52,6 +52,10 @@
 
 namespace pkv {
 
+// Build-time alternatives, kept for measuring the choices they stand for
+// (the defaults are the measured best): PKV_DEC_NW waves per workgroup,
+// PKV_DEC_NT=0 for cached instead of nontemporal K/V loads (8% slower),
+// PKV_DEC_PP=0 for one tile in flight per wave instead of two.
 #ifndef PKV_DEC_NW
 #define PKV_DEC_NW 4
 #endif

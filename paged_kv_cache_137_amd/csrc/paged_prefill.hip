@@ -56,6 +56,8 @@
 
 namespace pkv {
 
+// Build-time alternative for measuring the XCD-aware work-item mapping:
+// PKV_PRE_XCD=0 maps workgroup i to item i.
 #ifndef PKV_PRE_XCD
 #define PKV_PRE_XCD 1
 #endif
