@@ -400,6 +400,37 @@ __global__ __launch_bounds__(D) void decode_reduce_kernel(const DecodeArgs a) {
   const int t = threadIdx.x;
   const int64_t sh = (int64_t)s * a.num_heads + h;
   const int64_t base = sh * a.num_parts;
+  // Up to RP partitions: every (m, l) and partial value is loaded at once, so
+  // the merge waits for memory once.  The arithmetic and its order are the
+  // same either way.
+  constexpr int RP = 8;
+  if (nparts <= RP) {
+    float mp[RP], lp[RP], ap[RP];
+#pragma unroll
+    for (int p = 0; p < RP; ++p) {
+      if (p < nparts) {
+        const float2 ml = *reinterpret_cast<const float2*>(a.ws_ml + (base + p) * 2);
+        mp[p] = ml.x;
+        lp[p] = ml.y;
+        ap[p] = a.ws_acc[(base + p) * D + t];
+      }
+    }
+    float M = mp[0];
+#pragma unroll
+    for (int p = 1; p < RP; ++p)
+      if (p < nparts) M = fmaxf(M, mp[p]);
+    float Ls = 0.f, A = 0.f;
+#pragma unroll
+    for (int p = 0; p < RP; ++p) {
+      if (p < nparts) {
+        const float f = fast_exp2(mp[p] - M);
+        Ls = fmaf(lp[p], f, Ls);
+        A = fmaf(ap[p], f, A);
+      }
+    }
+    Out<O>::put(a.out, sh * D + t, A / Ls);
+    return;
+  }
   float M = a.ws_ml[base * 2];
   for (int p = 1; p < nparts; ++p) M = fmaxf(M, a.ws_ml[(base + p) * 2]);
   float Ls = 0.f, A = 0.f;
