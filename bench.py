@@ -105,7 +105,7 @@ def main() -> int:
     a = _args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if a.gpus != 1 or world != 1:
-        print("bench.py measures one MI355X: this build has no multi-GPU path "
+        print("bench.py measures one MI355X: the library runs on one GPU and has no multi-GPU path "
               "(--gpus must be 1).", file=sys.stderr)
         return 2
 
