@@ -6,8 +6,10 @@ A step is one decode step of the Llama-2-7B-shaped workload: 256 sequences,
 32 heads x 128, bf16, 16-token blocks, context lengths lognormal (median 600,
 sigma 0.8) clipped to [16, 4096], in shuffled physical blocks.  The step
   1. writes the 256 current tokens' K/V into their slots (kv_cache_write),
-  2. runs the per-partition decode kernel (512-token partitions),
-  3. runs the split-context reduce.
+  2. runs the plan and the persistent decode kernel, with the library's
+     automatic context partition (for 256 sequences x 8 head groups: no split),
+  3. runs the split-context reduce, which has nothing to do without a split
+     (--partition 512 times the split path and its reduce instead).
 Inputs are resident in HBM before the timed region starts.  One JSON line is
 printed.  value = KV bytes attended per step (sum of context lengths x 2 x heads
 x head_dim x 2 B) / wall time per step.
@@ -66,7 +68,8 @@ def _args():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--partition", type=int, default=512)
+    ap.add_argument("--partition", type=int, default=-1,
+                    help="decode partition in tokens; -1 (default) = the library's automatic choice, 0 = no split")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-mixed", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip the sharing and cached-prefix measurements")
@@ -145,6 +148,7 @@ def main() -> int:
     t["sm"] = up(slot_mapping(d.block_tables, np.arange(S), d.context_lens - 1))
     out = torch.empty((S, H, D), dtype=torch.bfloat16, device=dev)
     mcl = d.max_context_len
+    part_used = ops.decode_partition(S, H, mcl, a.partition)
     ws = torch.empty(max(1, ops.decode_workspace_bytes(S, H, D, mcl, a.partition)), dtype=torch.uint8, device=dev)
     dargs = (t["q"], t["kc"], t["vc"], t["bt"], t["cl"], d.scale, out)
     dkw = dict(max_context_len=mcl, partition_size=a.partition, workspace=ws)
@@ -204,8 +208,11 @@ def main() -> int:
         "data": "synthetic",
         "config": {
             "workload": "Llama-2-7B-shape paged decode step: 256 seqs, 32 heads x 128, bf16, 16-token blocks, "
-                        "ctx lognormal(600, 0.8) in [16, 4096], shuffled blocks, 512-token partitions + reduce",
+                        "ctx lognormal(600, 0.8) in [16, 4096], shuffled blocks, "
+                        + ("automatic partition" if a.partition == ops.PARTITION_AUTO else f"partition {a.partition}")
+                        + f" (resolved: {part_used or 'no split'})",
             "num_seqs": S, "num_heads": H, "head_dim": D, "block_size": 16, "partition_size": a.partition,
+            "partition_resolved": part_used,
             "sum_context_len": sum_ctx, "max_context_len": mcl, "num_blocks": d.num_blocks,
             "seed": W.config_seed(3),
         },
@@ -276,7 +283,8 @@ def mixed_step(a, dev, up):
     pout = torch.empty(pq.shape, dtype=torch.bfloat16, device=dev)
     dout = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
     mpl, mcl = int(p.prompt_lens.max()), d.max_context_len
-    ws = torch.empty(max(1, ops.decode_workspace_bytes(S, H, D, mcl, 512)), dtype=torch.uint8, device=dev)
+    ws = torch.empty(max(1, ops.decode_workspace_bytes(S, H, D, mcl, ops.PARTITION_AUTO)), dtype=torch.uint8,
+                     device=dev)
 
     def run(ev=None):
         if ev is not None:
@@ -287,8 +295,8 @@ def mixed_step(a, dev, up):
         ops.paged_attn_prefill(pq, pk, pv, ptab, plens, pout, max_prompt_len=mpl)
         if ev is not None:
             ev[2].record()
-        ops.paged_attn_decode(q, kc, vc, bt, cl, d.scale, dout, max_context_len=mcl, partition_size=512,
-                              workspace=ws)
+        ops.paged_attn_decode(q, kc, vc, bt, cl, d.scale, dout, max_context_len=mcl,
+                              partition_size=ops.PARTITION_AUTO, workspace=ws)
         if ev is not None:
             ev[3].record()
 
@@ -316,8 +324,8 @@ def mixed_step(a, dev, up):
         with torch.cuda.stream(side):
             ops.paged_attn_prefill(pq, pk, pv, ptab, plens, pout, max_prompt_len=mpl)
         ops.kv_cache_write(k_all, v_all, smd, kc, vc)
-        ops.paged_attn_decode(q, kc, vc, bt, cl, d.scale, dout, max_context_len=mcl, partition_size=512,
-                              workspace=ws)
+        ops.paged_attn_decode(q, kc, vc, bt, cl, d.scale, dout, max_context_len=mcl,
+                              partition_size=ops.PARTITION_AUTO, workspace=ws)
         main.wait_stream(side)
 
     for _ in range(a.warmup):
@@ -377,12 +385,15 @@ def opt13b_decode(a, dev, up):
     S, H, D = d.q.shape
     t = dict(q=up(d.q), kc=up(d.k_cache), vc=up(d.v_cache), bt=up(d.block_tables), cl=up(d.context_lens))
     out = torch.empty((S, H, D), dtype=torch.float16, device=dev)
-    ws = torch.empty(ops.decode_workspace_bytes(S, H, D, d.max_context_len, 512), dtype=torch.uint8, device=dev)
+    ws = torch.empty(ops.decode_workspace_bytes(S, H, D, d.max_context_len, ops.PARTITION_AUTO), dtype=torch.uint8,
+                     device=dev)
     ms = _time_events(lambda: ops.paged_attn_decode(t["q"], t["kc"], t["vc"], t["bt"], t["cl"], d.scale, out,
-                                                    max_context_len=d.max_context_len, partition_size=512,
-                                                    workspace=ws), a.warmup, a.steps)
+                                                    max_context_len=d.max_context_len,
+                                                    partition_size=ops.PARTITION_AUTO, workspace=ws),
+                      a.warmup, a.steps)
     nbytes = int(d.context_lens.sum()) * 2 * H * D * 2
-    return {"workload": "OPT-13B-shape decode step: 64 seqs, 40 heads x 128, fp16, ctx U[1, 2048], shuffled blocks",
+    return {"workload": "OPT-13B-shape decode step: 64 seqs, 40 heads x 128, fp16, ctx U[1, 2048], shuffled blocks, "
+                        f"automatic partition ({ops.decode_partition(S, H, d.max_context_len)} tokens)",
             "sum_context_len": int(d.context_lens.sum()), "ms": round(ms, 4),
             "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1), "frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
 

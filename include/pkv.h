@@ -63,6 +63,10 @@ extern "C" {
 
 typedef enum { PKV_F32 = 0, PKV_F16 = 1, PKV_BF16 = 2 } pkv_dtype;
 
+/* partition_size value that lets the library choose the context partition of
+ * the decode (see pkv_paged_attn_decode). */
+#define PKV_PARTITION_AUTO (-1)
+
 typedef enum {
   PKV_OK = 0,
   PKV_EINVAL = -1,     /* null pointer, bad size, misaligned pointer, failed PKV_VALIDATE check */
@@ -116,7 +120,9 @@ int pkv_kv_cache_write(const void* k, const void* v, const int64_t* slot_mapping
 
 /*
  * Workspace for pkv_paged_attn_decode, in bytes.  P = ceil(max_context_len /
- * partition_size), or 1 when partition_size == 0.  The workspace holds:
+ * partition_size), or 1 when partition_size == 0.  PKV_PARTITION_AUTO is
+ * resolved exactly as the decode resolves it for the same arguments.  The
+ * workspace holds:
  *   - a work counter (16 B);
  *   - the list of (sequence, partition) units (num_seqs * P int32);
  *   - when P > 1, the partial results of the split-context decode in float32
@@ -126,6 +132,17 @@ int pkv_kv_cache_write(const void* k, const void* v, const int64_t* slot_mapping
  */
 size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
                                   int32_t max_context_len, int32_t partition_size);
+
+/*
+ * The partition size a decode call uses for these arguments: partition_size
+ * itself, or what PKV_PARTITION_AUTO resolves to (0 = no split) for the plain
+ * decode (shared == 0) or the shared-prefix decode (shared != 0); see
+ * pkv_paged_attn_decode.  Host arithmetic only.  Returns -1 for an invalid
+ * shape (num_seqs < 0, num_heads <= 0 or max_context_len <= 0).  The value is
+ * not checked against the block size: the decode call does that.
+ */
+int32_t pkv_decode_partition(int32_t num_seqs, int32_t num_heads, int32_t max_context_len, int32_t partition_size,
+                             int32_t shared);
 
 /*
  * pkv_paged_attn_decode - attention of each sequence's current token over its
@@ -153,6 +170,15 @@ size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t h
  *                 is one workgroup.  A sequence spanning more than one partition
  *                 is merged by a second, reduce kernel (max-rescaled sum of the
  *                 partial results), in a fixed order.
+ *                 PKV_PARTITION_AUTO picks the size from the shape alone
+ *                 (num_seqs, num_heads, max_context_len): no split when
+ *                 num_seqs * ceil(num_heads / 4) >= 1024 (enough units to
+ *                 keep every CU busy); otherwise parts = ceil(1024 /
+ *                 (num_seqs * ceil(num_heads / 4))) and the size is
+ *                 ceil(max_context_len / parts) rounded up to a multiple of 32
+ *                 tokens, at least 256, with no split if that covers
+ *                 max_context_len.  The result
+ *                 depends neither on the block size nor on the device.
  *   workspace     device scratch of at least pkv_decode_workspace_bytes(...),
  *                 owned by the caller.  Calls that can run at the same time
  *                 (different streams) need separate workspaces.
@@ -206,7 +232,8 @@ int pkv_paged_attn_decode_reduce(const void* q, const void* k_cache, const void*
  * own, and a merge combines the partial results in a fixed order.  Nothing is
  * assumed about the tables: sharing is found on the device each call, and a
  * batch without it gives the plain decode's partitions.  Results are
- * deterministic, bit for bit.
+ * deterministic, bit for bit.  Here PKV_PARTITION_AUTO means 512-token
+ * partitions.
  */
 size_t pkv_decode_shared_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
                                          int32_t max_context_len, int32_t partition_size);

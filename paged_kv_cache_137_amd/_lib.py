@@ -14,6 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libpkv.so")
 
 PKV_F32, PKV_F16, PKV_BF16 = 0, 1, 2
+PKV_PARTITION_AUTO = -1  # the library picks the decode's context partition
 PKV_OK, PKV_EINVAL, PKV_ENOTSUP, PKV_ELAUNCH, PKV_EDEVICE, PKV_EWORKSPACE = 0, -1, -2, -3, -4, -5
 
 # Every function include/pkv.h declares, with its ctypes signature.
@@ -25,6 +26,7 @@ SIGNATURES = {
     "pkv_check_device": ([], ctypes.c_int),
     "pkv_kv_cache_write": ([_vp, _vp, _vp, _i64, _vp, _vp, _vp, _vp], ctypes.c_int),
     "pkv_decode_workspace_bytes": ([_i32, _i32, _i32, _i32, _i32], _sz),
+    "pkv_decode_partition": ([_i32, _i32, _i32, _i32, _i32], _i32),
     "pkv_paged_attn_decode": (_DECODE_ARGS, ctypes.c_int),
     "pkv_paged_attn_decode_partial": (_DECODE_ARGS, ctypes.c_int),
     "pkv_paged_attn_decode_reduce": (_DECODE_ARGS, ctypes.c_int),

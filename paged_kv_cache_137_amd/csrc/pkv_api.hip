@@ -113,6 +113,29 @@ DecodePlan plan_decode(int32_t num_seqs, int32_t num_heads, int32_t head_dim, in
 
 enum Stage { kPartial = 1, kReduce = 2, kBoth = 3 };
 
+// The partition size used when the caller passes PKV_PARTITION_AUTO.  With
+// enough (sequence, head group) units to keep every CU busy a few times over,
+// contexts are not split: no partial results are written and no reduce runs.
+// Otherwise the longest context is cut into ceil(target / units) partitions,
+// whose size is rounded up to a multiple of 32 tokens (so the choice does not
+// depend on the block size; the rounding can only lower the count) and kept
+// at 256 tokens or more.  The shared-prefix decode uses 512-token partitions.
+constexpr int32_t kAutoHeadsPerUnit = 4;   // heads that one decode unit covers
+constexpr int64_t kAutoTargetUnits = 1024;  // four units per CU on a 256-CU part
+int32_t resolve_partition(int32_t partition_size, int32_t num_seqs, int32_t num_heads, int32_t max_context_len,
+                          bool shared) {
+  if (partition_size != PKV_PARTITION_AUTO) return partition_size;
+  if (shared) return 512;
+  const int64_t units = (int64_t)num_seqs * ((num_heads + kAutoHeadsPerUnit - 1) / kAutoHeadsPerUnit);
+  if (units <= 0 || units >= kAutoTargetUnits) return 0;
+  const int64_t parts = (kAutoTargetUnits + units - 1) / units;
+  int64_t size = (max_context_len + parts - 1) / parts;
+  size = (size + 31) / 32 * 32;
+  if (size < 256) size = 256;
+  if (size >= max_context_len) return 0;
+  return (int32_t)(size < 4096 ? size : 4096);
+}
+
 int decode_impl(int stages, bool shared, const void* q, const void* k_cache, const void* v_cache,
                 const pkv_cache_desc* desc,
                 const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
@@ -124,6 +147,7 @@ int decode_impl(int stages, bool shared, const void* q, const void* k_cache, con
   const int32_t bsz = desc->block_size;
   if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * bsz) return PKV_EINVAL;
   if (out_dtype != PKV_F32 && out_dtype != desc->dtype) return PKV_ENOTSUP;
+  partition_size = resolve_partition(partition_size, num_seqs, desc->num_heads, max_context_len, shared);
   if (partition_size != 0 && (partition_size % bsz != 0 || partition_size < 16 || partition_size > 4096))
     return PKV_EINVAL;
   if (num_seqs == 0) return PKV_OK;
@@ -265,13 +289,23 @@ int pkv_kv_cache_write(const void* k, const void* v, const int64_t* slot_mapping
 
 size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim, int32_t max_context_len,
                                   int32_t partition_size) {
-  if (num_seqs <= 0 || num_heads <= 0 || head_dim <= 0 || max_context_len <= 0 || partition_size < 0) return 0;
+  if (num_seqs <= 0 || num_heads <= 0 || head_dim <= 0 || max_context_len <= 0) return 0;
+  partition_size = resolve_partition(partition_size, num_seqs, num_heads, max_context_len, false);
+  if (partition_size < 0) return 0;
   return plan_decode(num_seqs, num_heads, head_dim, max_context_len, partition_size).ws_bytes;
+}
+
+int32_t pkv_decode_partition(int32_t num_seqs, int32_t num_heads, int32_t max_context_len, int32_t partition_size,
+                             int32_t shared) {
+  if (num_seqs < 0 || num_heads <= 0 || max_context_len <= 0) return -1;
+  return resolve_partition(partition_size, num_seqs, num_heads, max_context_len, shared != 0);
 }
 
 size_t pkv_decode_shared_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
                                          int32_t max_context_len, int32_t partition_size) {
-  if (num_seqs <= 0 || num_heads <= 0 || head_dim <= 0 || max_context_len <= 0 || partition_size < 0) return 0;
+  if (num_seqs <= 0 || num_heads <= 0 || head_dim <= 0 || max_context_len <= 0) return 0;
+  partition_size = resolve_partition(partition_size, num_seqs, num_heads, max_context_len, true);
+  if (partition_size < 0) return 0;
   return plan_decode(num_seqs, num_heads, head_dim, max_context_len, partition_size, kBlock, true).ws_bytes;
 }
 

@@ -17,7 +17,8 @@ from ._lib import CacheDesc, check, lib
 
 BLOCK_SIZE = 16           # the default block size (tokens per block)
 BLOCK_SIZES = (8, 16, 32)  # block sizes the library is built for
-DEFAULT_PARTITION = 512
+PARTITION_AUTO = _lib.PKV_PARTITION_AUTO  # the library picks the partition from the batch shape
+DEFAULT_PARTITION = PARTITION_AUTO
 
 _DT = {torch.float32: _lib.PKV_F32, torch.float16: _lib.PKV_F16, torch.bfloat16: _lib.PKV_BF16}
 
@@ -102,6 +103,12 @@ def decode_shared_workspace_bytes(num_seqs: int, num_heads: int, head_dim: int, 
                                                        partition_size))
 
 
+def decode_partition(num_seqs: int, num_heads: int, max_context_len: int,
+                     partition_size: int = DEFAULT_PARTITION, shared: bool = False) -> int:
+    """The partition size (0 = no split) a decode call uses for these arguments."""
+    return int(lib().pkv_decode_partition(num_seqs, num_heads, max_context_len, partition_size, int(shared)))
+
+
 def _decode_call(fn_name, q, k_cache, v_cache, block_tables, context_lens, scale, out,
                  max_context_len, partition_size, workspace):
     _need(k_cache, "k_cache", dim=4)
@@ -146,7 +153,10 @@ def paged_attn_decode(q, k_cache, v_cache, block_tables, context_lens, scale, ou
 
     max_context_len bounds every context_lens entry.  By default it is the table
     capacity (max_blocks_per_seq * block_size).  partition_size = 0 disables the
-    split-context path.  Without a workspace, one is allocated through torch.
+    split-context path; PARTITION_AUTO (the default) lets the library choose from
+    the batch shape: no split when num_seqs * ceil(num_heads / 4) >= 1024, else
+    partitions of at least 256 tokens that give that many units.  Without a
+    workspace, one is allocated through torch.
     """
     return _decode_call("pkv_paged_attn_decode", q, k_cache, v_cache, block_tables, context_lens, scale, out,
                         max_context_len, partition_size, workspace)

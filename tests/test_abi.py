@@ -83,6 +83,46 @@ def test_shared_decode_workspace_sizing(lib):
     assert lib.pkv_decode_shared_workspace_bytes(S, H, D, 4096, 512) > lib.pkv_decode_workspace_bytes(S, H, D, 4096, 512)
 
 
+def _auto_rule(S, H, max_ctx):
+    """The automatic partition as the header states it (0 = no split)."""
+    units = S * -(-H // 4)
+    if units == 0 or units >= 1024:
+        return 0
+    parts = -(-1024 // units)
+    size = max(256, -(-(-(-max_ctx // parts)) // 32) * 32)
+    return 0 if size >= max_ctx else min(size, 4096)
+
+
+def test_auto_partition(lib):
+    auto = _lib.PKV_PARTITION_AUTO
+    shapes = [(256, 32, 4096), (64, 40, 2041), (192, 32, 4096), (512, 40, 1276), (2, 8, 100000), (1, 1, 100),
+              (0, 8, 100), (255, 4, 8192), (256, 4, 8192), (3, 7, 5000), (100, 1, 65536), (1, 64, 300)]
+    for S, H, mc in shapes:
+        want = _auto_rule(S, H, mc)
+        got = lib.pkv_decode_partition(S, H, mc, auto, 0)
+        assert got == want, (S, H, mc, got, want)
+        assert got == 0 or (got % 32 == 0 and 256 <= got <= 4096 and got < mc)
+        # the shared-prefix decode resolves it to 512; explicit sizes pass through
+        assert lib.pkv_decode_partition(S, H, mc, auto, 1) == 512
+        assert lib.pkv_decode_partition(S, H, mc, 1024, 0) == 1024
+        assert lib.pkv_decode_partition(S, H, mc, 0, 1) == 0
+        if S:  # the sizing calls resolve it the same way
+            assert lib.pkv_decode_workspace_bytes(S, H, 128, mc, auto) == lib.pkv_decode_workspace_bytes(
+                S, H, 128, mc, want)
+            assert lib.pkv_decode_shared_workspace_bytes(S, H, 128, mc, auto) == (
+                lib.pkv_decode_shared_workspace_bytes(S, H, 128, mc, 512))
+    # where it splits, the longest context gets ceil(1024 / units) partitions,
+    # fewer only through the rounding up to 32 tokens (or the 256-token floor)
+    for S, H, mc in [(64, 40, 2041), (2, 8, 100000), (3, 7, 5000)]:
+        part = lib.pkv_decode_partition(S, H, mc, auto, 0)
+        units0 = S * -(-H // 4)
+        parts = -(-1024 // units0)
+        assert -(-mc // part) <= parts
+    assert lib.pkv_decode_partition(-1, 8, 100, auto, 0) == -1
+    assert lib.pkv_decode_partition(4, 0, 100, auto, 0) == -1
+    assert lib.pkv_decode_partition(4, 8, 0, auto, 0) == -1
+
+
 def test_bad_arguments_rejected_before_any_launch(lib):
     desc = _lib.CacheDesc(64, 4, 128, 16, _lib.PKV_BF16)
     null = ctypes.c_void_p(0)

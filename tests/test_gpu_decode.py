@@ -49,8 +49,9 @@ def test_decode_config_parity(cfg):
 
 
 def test_decode_config3_bench_launch():
-    """Config 3 at full size in the launch configuration the benchmark times:
-    write the 256 current tokens, then partitions of 512 plus the reduce."""
+    """Config 3 at full size: write the 256 current tokens, then partitions of
+    512 plus the reduce, and the launch the benchmark times (the automatic
+    partition, which for 256 sequences x 8 head groups is no split)."""
     print("decode parity config 3 (write + partial + reduce)", flush=True)
     d = W.decode_config(3, with_new_tokens=True)
     t = upload_decode(d)
@@ -73,6 +74,32 @@ def test_decode_config3_bench_launch():
     ops.paged_attn_decode(*args[:-1], whole, **kw)
     assert torch.equal(whole, out32)
     assert (d.context_lens > 512).sum() > 0
+    # the benchmark's launch: automatic partition (no split here), partial then
+    # reduce (a no-op without a split)
+    assert ops.decode_partition(d.num_seqs, 32, d.max_context_len) == 0
+    auto = torch.empty_like(out32)
+    akw = dict(max_context_len=d.max_context_len, partition_size=ops.PARTITION_AUTO)
+    ops.paged_attn_decode_partial(*args[:-1], auto, **akw)
+    ops.paged_attn_decode_reduce(*args[:-1], auto, **akw)
+    _check(d, auto, None, seqs, kc, vc)
+    nosplit = torch.empty_like(out32)
+    ops.paged_attn_decode(*args[:-1], nosplit, max_context_len=d.max_context_len, partition_size=0)
+    assert torch.equal(auto, nosplit)
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+def test_decode_auto_partition_splits_small_batches(dt):
+    """Few sequences with long contexts: the automatic partition splits them, and
+    the result is that explicit partition's, bit for bit."""
+    lens = [4096, 3000, 1, 2049, 700, 4095, 16, 2500]
+    d = _batch(71, dt, lens, H=8)
+    part = ops.decode_partition(d.num_seqs, 8, d.max_context_len)
+    print(f"auto partition {dt}: {part}", flush=True)
+    assert part == 256  # 8 x 2 units -> 64 partitions of the longest context, floored at 256 tokens
+    t = upload_decode(d)
+    auto = run_decode(ops, t, d, "f32", partition_size=ops.PARTITION_AUTO)
+    _check(d, auto, None, list(range(d.num_seqs)))
+    assert torch.equal(auto, run_decode(ops, t, d, "f32", partition_size=part))
 
 
 def _batch(seed, dt, lens, H=8, D=128, **kw):
