@@ -304,7 +304,7 @@ def make_prefill(seed: int, dtype: str, num_heads: int, head_dim: int, prompt_le
 CONFIG_NAMES = {
     1: "tiny decode, fp32: 4 seqs, 4x64, ctx {1,17,100,300}, 64-block pool",
     2: "OPT-13B-shape decode, fp16: 64 seqs, 40x128, ctx U[1,2048]",
-    3: "Llama-2-7B-shape decode, bf16: 256 seqs, 32x128, ctx lognormal(600,0.8) in [16,4096], 512-token partitions",
+    3: "Llama-2-7B-shape decode, bf16: 256 seqs, 32x128, ctx lognormal(600,0.8) in [16,4096]",
     4: "block-sharing decode, fp16: 40x128, 128 prompts x 4 samples, CoW partial block",
     5: "mixed step, bf16: 32x128, 8 prompts U[128,2048] prefill + 192 decodes lognormal(800,0.8)",
 }
