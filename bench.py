@@ -425,11 +425,16 @@ def sharing_step(a, dev, up):
     dec_ms = _time_events(lambda: ops.paged_attn_decode(t["q"], t["kc"], t["vc"], t["bt"], t["cl"], d.scale, out,
                                                         max_context_len=d.max_context_len, partition_size=512,
                                                         workspace=ws), a.warmup, a.steps)
-    wss = torch.empty(ops.decode_shared_workspace_bytes(S, H, D, d.max_context_len, 512), dtype=torch.uint8,
-                      device=dev)
+    # The plain decode at 512-token partitions (faster on this batch than its
+    # automatic choice, no split, which reads a sample's private blocks with the
+    # cached loads of its shared first partition); the shared-prefix decode at
+    # its automatic choice (no split).
+    wss = torch.empty(ops.decode_shared_workspace_bytes(S, H, D, d.max_context_len, ops.PARTITION_AUTO),
+                      dtype=torch.uint8, device=dev)
     shr_ms = _time_events(lambda: ops.paged_attn_decode_shared(t["q"], t["kc"], t["vc"], t["bt"], t["cl"], d.scale,
                                                                out, max_context_len=d.max_context_len,
-                                                               partition_size=512, workspace=wss), a.warmup, a.steps)
+                                                               partition_size=ops.PARTITION_AUTO, workspace=wss),
+                          a.warmup, a.steps)
     used = np.zeros((d.num_blocks, 16), dtype=bool)
     for s_ in range(S):
         n = int(d.context_lens[s_])

@@ -136,8 +136,8 @@ size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t h
 /*
  * The partition size a decode call uses for these arguments: partition_size
  * itself, or what PKV_PARTITION_AUTO resolves to (0 = no split) for the plain
- * decode (shared == 0) or the shared-prefix decode (shared != 0); see
- * pkv_paged_attn_decode.  Host arithmetic only.  Returns -1 for an invalid
+ * decode (shared == 0) or the shared-prefix decode (shared != 0), which follow
+ * the same rule; see pkv_paged_attn_decode.  Host arithmetic only.  Returns -1 for an invalid
  * shape (num_seqs < 0, num_heads <= 0 or max_context_len <= 0).  The value is
  * not checked against the block size: the decode call does that.
  */
@@ -232,8 +232,8 @@ int pkv_paged_attn_decode_reduce(const void* q, const void* k_cache, const void*
  * own, and a merge combines the partial results in a fixed order.  Nothing is
  * assumed about the tables: sharing is found on the device each call, and a
  * batch without it gives the plain decode's partitions.  Results are
- * deterministic, bit for bit.  Here PKV_PARTITION_AUTO means 512-token
- * partitions.
+ * deterministic, bit for bit.  PKV_PARTITION_AUTO resolves as for
+ * pkv_paged_attn_decode.
  */
 size_t pkv_decode_shared_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
                                          int32_t max_context_len, int32_t partition_size);

@@ -119,13 +119,13 @@ enum Stage { kPartial = 1, kReduce = 2, kBoth = 3 };
 // Otherwise the longest context is cut into ceil(target / units) partitions,
 // whose size is rounded up to a multiple of 32 tokens (so the choice does not
 // depend on the block size; the rounding can only lower the count) and kept
-// at 256 tokens or more.  The shared-prefix decode uses 512-token partitions.
+// at 256 tokens or more.  The shared-prefix decode follows the same rule.
 constexpr int32_t kAutoHeadsPerUnit = 4;   // heads that one decode unit covers
 constexpr int64_t kAutoTargetUnits = 1024;  // four units per CU on a 256-CU part
 int32_t resolve_partition(int32_t partition_size, int32_t num_seqs, int32_t num_heads, int32_t max_context_len,
                           bool shared) {
+  (void)shared;  // measured: the same choice suits both decodes
   if (partition_size != PKV_PARTITION_AUTO) return partition_size;
-  if (shared) return 512;
   const int64_t units = (int64_t)num_seqs * ((num_heads + kAutoHeadsPerUnit - 1) / kAutoHeadsPerUnit);
   if (units <= 0 || units >= kAutoTargetUnits) return 0;
   const int64_t parts = (kAutoTargetUnits + units - 1) / units;

@@ -102,15 +102,15 @@ def test_auto_partition(lib):
         got = lib.pkv_decode_partition(S, H, mc, auto, 0)
         assert got == want, (S, H, mc, got, want)
         assert got == 0 or (got % 32 == 0 and 256 <= got <= 4096 and got < mc)
-        # the shared-prefix decode resolves it to 512; explicit sizes pass through
-        assert lib.pkv_decode_partition(S, H, mc, auto, 1) == 512
+        # the shared-prefix decode follows the same rule; explicit sizes pass through
+        assert lib.pkv_decode_partition(S, H, mc, auto, 1) == want
         assert lib.pkv_decode_partition(S, H, mc, 1024, 0) == 1024
         assert lib.pkv_decode_partition(S, H, mc, 0, 1) == 0
         if S:  # the sizing calls resolve it the same way
             assert lib.pkv_decode_workspace_bytes(S, H, 128, mc, auto) == lib.pkv_decode_workspace_bytes(
                 S, H, 128, mc, want)
             assert lib.pkv_decode_shared_workspace_bytes(S, H, 128, mc, auto) == (
-                lib.pkv_decode_shared_workspace_bytes(S, H, 128, mc, 512))
+                lib.pkv_decode_shared_workspace_bytes(S, H, 128, mc, want))
     # where it splits, the longest context gets ceil(1024 / units) partitions,
     # fewer only through the rounding up to 32 tokens (or the 256-token floor)
     for S, H, mc in [(64, 40, 2041), (2, 8, 100000), (3, 7, 5000)]:
