@@ -2,7 +2,7 @@
 
 Each case draws its own shape (dtype, head_dim, block size, heads, batch),
 context or prompt lengths from a mix of edge values and random ones, a
-partition size, and a random block layout in which some neighbouring sequences
+partition size (or the library's automatic choice), and a random block layout in which some neighbouring sequences
 share leading blocks.  The plain decode and the shared-prefix decode must both
 match the oracle on every sequence (1e-5 for fp32 inputs, 5e-3 for 16-bit
 inputs, on fp32 outputs); the cached-prefix prefill must match the oracle's
@@ -34,7 +34,7 @@ def _random_decode(seed: int) -> tuple[W.DecodeInputs, int]:
     B = int(rng.choice([8, 16, 32]))
     H = int(rng.integers(1, 9))
     S = int(rng.integers(1, 41))
-    part = int(rng.choice([0, 256, 512, 1024]))
+    part = int(rng.choice([0, 256, 512, 1024, ops.PARTITION_AUTO]))
     lens = [int(rng.choice(EDGE)) if rng.random() < 0.5 else int(rng.integers(1, 3001)) for _ in range(S)]
     # Block ids: windows of four sequences may share a prefix of their leading blocks.
     nxt = 0
