@@ -171,13 +171,14 @@ int32_t pkv_decode_partition(int32_t num_seqs, int32_t num_heads, int32_t max_co
  *                 is merged by a second, reduce kernel (max-rescaled sum of the
  *                 partial results), in a fixed order.
  *                 PKV_PARTITION_AUTO picks the size from the shape alone
- *                 (num_seqs, num_heads, max_context_len): no split when
- *                 num_seqs * ceil(num_heads / 4) >= 1024 (enough units to
- *                 keep every CU busy); otherwise parts = ceil(1024 /
- *                 (num_seqs * ceil(num_heads / 4))) and the size is
- *                 ceil(max_context_len / parts) rounded up to a multiple of 32
- *                 tokens, at least 256, with no split if that covers
- *                 max_context_len.  The result
+ *                 (num_seqs, num_heads, max_context_len).  With units =
+ *                 num_seqs * ceil(num_heads / 4): no split when units >= 1024
+ *                 (enough to keep every CU busy) and max_context_len <= 4096;
+ *                 otherwise parts = ceil(1024 / units) (1 if units >= 1024)
+ *                 and the size is ceil(max_context_len / parts) rounded up to
+ *                 a multiple of 32 tokens, at least 256 and at most 2048
+ *                 (which bounds the longest unit), with no split if that
+ *                 covers max_context_len.  The result
  *                 depends neither on the block size nor on the device.
  *   workspace     device scratch of at least pkv_decode_workspace_bytes(...),
  *                 owned by the caller.  Calls that can run at the same time

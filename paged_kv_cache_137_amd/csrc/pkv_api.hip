@@ -115,25 +115,33 @@ enum Stage { kPartial = 1, kReduce = 2, kBoth = 3 };
 
 // The partition size used when the caller passes PKV_PARTITION_AUTO.  With
 // enough (sequence, head group) units to keep every CU busy a few times over,
-// contexts are not split: no partial results are written and no reduce runs.
-// Otherwise the longest context is cut into ceil(target / units) partitions,
-// whose size is rounded up to a multiple of 32 tokens (so the choice does not
-// depend on the block size; the rounding can only lower the count) and kept
-// at 256 tokens or more.  The shared-prefix decode follows the same rule.
-constexpr int32_t kAutoHeadsPerUnit = 4;   // heads that one decode unit covers
+// and no context longer than kAutoMaxUnsplit tokens, contexts are not split: no
+// partial results are written and no reduce runs.  Otherwise the longest
+// context is cut into ceil(target / units) partitions (one when the units
+// already suffice), whose size is rounded up to a multiple of 32 tokens (so the
+// choice does not depend on the block size; the rounding can only lower the
+// count), kept at 256 tokens or more and at kAutoMaxPartition or fewer.  The
+// cap bounds the longest unit: one very long context among many short ones
+// would otherwise be one unit far larger than a CU's share of the batch.  The
+// shared-prefix decode follows the same rule.
+constexpr int32_t kAutoHeadsPerUnit = 4;    // heads that one decode unit covers
 constexpr int64_t kAutoTargetUnits = 1024;  // four units per CU on a 256-CU part
+constexpr int64_t kAutoMaxUnsplit = 4096;   // longest context left whole
+constexpr int64_t kAutoMaxPartition = 2048;
 int32_t resolve_partition(int32_t partition_size, int32_t num_seqs, int32_t num_heads, int32_t max_context_len,
                           bool shared) {
   (void)shared;  // measured: the same choice suits both decodes
   if (partition_size != PKV_PARTITION_AUTO) return partition_size;
   const int64_t units = (int64_t)num_seqs * ((num_heads + kAutoHeadsPerUnit - 1) / kAutoHeadsPerUnit);
-  if (units <= 0 || units >= kAutoTargetUnits) return 0;
-  const int64_t parts = (kAutoTargetUnits + units - 1) / units;
+  if (units <= 0) return 0;
+  if (units >= kAutoTargetUnits && max_context_len <= kAutoMaxUnsplit) return 0;
+  const int64_t parts = units >= kAutoTargetUnits ? 1 : (kAutoTargetUnits + units - 1) / units;
   int64_t size = (max_context_len + parts - 1) / parts;
   size = (size + 31) / 32 * 32;
   if (size < 256) size = 256;
+  if (size > kAutoMaxPartition) size = kAutoMaxPartition;
   if (size >= max_context_len) return 0;
-  return (int32_t)(size < 4096 ? size : 4096);
+  return (int32_t)size;
 }
 
 int decode_impl(int stages, bool shared, const void* q, const void* k_cache, const void* v_cache,

@@ -154,8 +154,9 @@ def paged_attn_decode(q, k_cache, v_cache, block_tables, context_lens, scale, ou
     max_context_len bounds every context_lens entry.  By default it is the table
     capacity (max_blocks_per_seq * block_size).  partition_size = 0 disables the
     split-context path; PARTITION_AUTO (the default) lets the library choose from
-    the batch shape: no split when num_seqs * ceil(num_heads / 4) >= 1024, else
-    partitions of at least 256 tokens that give that many units.  Without a
+    the batch shape: no split when num_seqs * ceil(num_heads / 4) >= 1024 and no
+    context exceeds 4096 tokens, else partitions of 256 to 2048 tokens that give
+    about that many units (decode_partition reports the choice).  Without a
     workspace, one is allocated through torch.
     """
     return _decode_call("pkv_paged_attn_decode", q, k_cache, v_cache, block_tables, context_lens, scale, out,

@@ -86,22 +86,24 @@ def test_shared_decode_workspace_sizing(lib):
 def _auto_rule(S, H, max_ctx):
     """The automatic partition as the header states it (0 = no split)."""
     units = S * -(-H // 4)
-    if units == 0 or units >= 1024:
+    if units == 0 or (units >= 1024 and max_ctx <= 4096):
         return 0
-    parts = -(-1024 // units)
-    size = max(256, -(-(-(-max_ctx // parts)) // 32) * 32)
-    return 0 if size >= max_ctx else min(size, 4096)
+    parts = 1 if units >= 1024 else -(-1024 // units)
+    size = min(2048, max(256, -(-(-(-max_ctx // parts)) // 32) * 32))
+    return 0 if size >= max_ctx else size
 
 
 def test_auto_partition(lib):
     auto = _lib.PKV_PARTITION_AUTO
     shapes = [(256, 32, 4096), (64, 40, 2041), (192, 32, 4096), (512, 40, 1276), (2, 8, 100000), (1, 1, 100),
-              (0, 8, 100), (255, 4, 8192), (256, 4, 8192), (3, 7, 5000), (100, 1, 65536), (1, 64, 300)]
+              (0, 8, 100), (255, 4, 8192), (256, 4, 8192), (3, 7, 5000), (100, 1, 65536), (1, 64, 300),
+              (256, 32, 4097), (256, 32, 32768), (1024, 8, 2048), (8, 32, 4096)]
     for S, H, mc in shapes:
         want = _auto_rule(S, H, mc)
         got = lib.pkv_decode_partition(S, H, mc, auto, 0)
         assert got == want, (S, H, mc, got, want)
-        assert got == 0 or (got % 32 == 0 and 256 <= got <= 4096 and got < mc)
+        assert got == 0 or (got % 32 == 0 and 256 <= got <= 2048 and got < mc)
+        assert got != 0 or mc <= 4096 or S * -(-H // 4) == 0  # long contexts are always split
         # the shared-prefix decode follows the same rule; explicit sizes pass through
         assert lib.pkv_decode_partition(S, H, mc, auto, 1) == want
         assert lib.pkv_decode_partition(S, H, mc, 1024, 0) == 1024
@@ -113,7 +115,7 @@ def test_auto_partition(lib):
                 lib.pkv_decode_shared_workspace_bytes(S, H, 128, mc, want))
     # where it splits, the longest context gets ceil(1024 / units) partitions,
     # fewer only through the rounding up to 32 tokens (or the 256-token floor)
-    for S, H, mc in [(64, 40, 2041), (2, 8, 100000), (3, 7, 5000)]:
+    for S, H, mc in [(64, 40, 2041), (3, 7, 5000)]:
         part = lib.pkv_decode_partition(S, H, mc, auto, 0)
         units0 = S * -(-H // 4)
         parts = -(-1024 // units0)

@@ -102,6 +102,22 @@ def test_decode_auto_partition_splits_small_batches(dt):
     assert torch.equal(auto, run_decode(ops, t, d, "f32", partition_size=part))
 
 
+def test_decode_auto_partition_bounds_long_contexts():
+    """A large batch with one long context: enough units to leave contexts whole,
+    but the 9,000-token context is still cut into 2,048-token partitions (so it
+    is not one unit many times a CU's share); bit for bit that explicit size."""
+    lens = [9000] + [16 + (37 * i) % 200 for i in range(1, 256)]
+    d = _batch(73, "bf16", lens, H=16)
+    part = ops.decode_partition(d.num_seqs, 16, d.max_context_len)
+    print(f"auto partition, 256 seqs, max ctx {d.max_context_len}: {part}", flush=True)
+    assert part == 2048
+    assert ops.decode_partition(d.num_seqs, 16, 4096) == 0  # the same batch with contexts <= 4096: no split
+    t = upload_decode(d)
+    auto = run_decode(ops, t, d, "f32", partition_size=ops.PARTITION_AUTO)
+    _check(d, auto, None, [0, 1, 2, 100, 255])
+    assert torch.equal(auto, run_decode(ops, t, d, "f32", partition_size=2048))
+
+
 def _batch(seed, dt, lens, H=8, D=128, **kw):
     return W.make_decode(seed, dt, H, D, lens, **kw)
 
