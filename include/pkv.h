@@ -178,7 +178,10 @@ int32_t pkv_decode_partition(int32_t num_seqs, int32_t num_heads, int32_t max_co
  *                 and the size is ceil(max_context_len / parts) rounded up to
  *                 a multiple of 32 tokens, at least 256 and at most 2048
  *                 (which bounds the longest unit), with no split if that
- *                 covers max_context_len.  The result
+ *                 covers max_context_len.  The rule does not see the context
+ *                 lengths themselves: for a large batch of nearly empty
+ *                 contexts beside one of up to 4096 tokens, an explicit size
+ *                 (e.g. 512) balances better.  The result
  *                 depends neither on the block size nor on the device.
  *   workspace     device scratch of at least pkv_decode_workspace_bytes(...),
  *                 owned by the caller.  Calls that can run at the same time
