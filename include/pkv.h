@@ -145,6 +145,22 @@ int32_t pkv_decode_partition(int32_t num_seqs, int32_t num_heads, int32_t max_co
                              int32_t shared);
 
 /*
+ * A partition size for pkv_paged_attn_decode (and the shared-prefix decode)
+ * chosen from the context lengths themselves, for callers that hold them on
+ * the host (a scheduler does).  context_lens: HOST int32 [num_seqs], each >= 1.
+ * With G = ceil(num_heads / 4) head groups and share = sum(context_lens) * G /
+ * 256 (one CU's part of the batch): 0 (no split) when num_seqs * G >= 1024 and
+ * the longest context is at most share; otherwise about share / 2 rounded up to
+ * a multiple of 32, no larger than what PKV_PARTITION_AUTO gives a batch of
+ * fewer than 1024 units, between 512 (256 for fewer than 1024 units) and 2048
+ * tokens, and 0 if that covers the longest context.  Unlike PKV_PARTITION_AUTO it splits a large batch of nearly
+ * empty contexts beside one long one.  Pass the result as partition_size, to
+ * the workspace sizing call as well.  Host arithmetic only; returns -1 for
+ * num_seqs < 0, num_heads <= 0, a null pointer or a length below 1.
+ */
+int32_t pkv_decode_partition_for_lengths(const int32_t* context_lens, int32_t num_seqs, int32_t num_heads);
+
+/*
  * pkv_paged_attn_decode - attention of each sequence's current token over its
  * whole cached context, gathered block by block through its block table.
  *

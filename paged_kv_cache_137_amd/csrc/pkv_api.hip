@@ -309,6 +309,35 @@ int32_t pkv_decode_partition(int32_t num_seqs, int32_t num_heads, int32_t max_co
   return resolve_partition(partition_size, num_seqs, num_heads, max_context_len, shared != 0);
 }
 
+int32_t pkv_decode_partition_for_lengths(const int32_t* context_lens, int32_t num_seqs, int32_t num_heads) {
+  if (num_seqs < 0 || num_heads <= 0 || (num_seqs > 0 && context_lens == nullptr)) return -1;
+  int64_t total = 0, longest = 0;
+  for (int32_t s = 0; s < num_seqs; ++s) {
+    if (context_lens[s] < 1) return -1;
+    total += context_lens[s];
+    longest = context_lens[s] > longest ? context_lens[s] : longest;
+  }
+  if (num_seqs == 0) return 0;
+  // Each unit covers kAutoHeadsPerUnit heads of one partition; with G head
+  // groups a CU's share of the batch is total * G / 256 unit-tokens.  Contexts
+  // stay whole when the batch has the units and its longest context is at most
+  // one CU's share; otherwise partitions of about half a share, up to
+  // kAutoMaxPartition tokens and at least 512 (256 for a batch of few units):
+  // below that, partial results and merges cost more than the balance gains.
+  const int64_t groups = (num_heads + kAutoHeadsPerUnit - 1) / kAutoHeadsPerUnit;
+  const int64_t share = total * groups / 256;
+  if ((int64_t)num_seqs * groups >= kAutoTargetUnits && longest <= share) return 0;
+  int64_t size = (share / 2 + 31) / 32 * 32;
+  if (num_seqs * groups < kAutoTargetUnits) {  // few units: as many as the shape rule makes, at least
+    const int32_t by_shape = resolve_partition(PKV_PARTITION_AUTO, num_seqs, num_heads, (int32_t)longest, false);
+    if (by_shape > 0 && by_shape < size) size = by_shape;
+  }
+  const int64_t floor = num_seqs * groups < kAutoTargetUnits ? 256 : 512;
+  if (size < floor) size = floor;
+  if (size > kAutoMaxPartition) size = kAutoMaxPartition;
+  return size >= longest ? 0 : (int32_t)size;
+}
+
 size_t pkv_decode_shared_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
                                          int32_t max_context_len, int32_t partition_size) {
   if (num_seqs <= 0 || num_heads <= 0 || head_dim <= 0 || max_context_len <= 0) return 0;

@@ -109,6 +109,18 @@ def decode_partition(num_seqs: int, num_heads: int, max_context_len: int,
     return int(lib().pkv_decode_partition(num_seqs, num_heads, max_context_len, partition_size, int(shared)))
 
 
+def decode_partition_for_lengths(context_lens, num_heads: int) -> int:
+    """A partition size chosen from the context lengths themselves (host values:
+    a sequence of ints or a CPU array), for callers that know them; 0 = no split."""
+    import numpy as np
+
+    lens = np.ascontiguousarray(np.asarray(context_lens, dtype=np.int32))
+    if lens.ndim != 1:
+        raise ValueError("context_lens must be one-dimensional")
+    return int(lib().pkv_decode_partition_for_lengths(lens.ctypes.data if lens.size else None, int(lens.size),
+                                                      int(num_heads)))
+
+
 def _decode_call(fn_name, q, k_cache, v_cache, block_tables, context_lens, scale, out,
                  max_context_len, partition_size, workspace):
     _need(k_cache, "k_cache", dim=4)

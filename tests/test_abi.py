@@ -125,6 +125,42 @@ def test_auto_partition(lib):
     assert lib.pkv_decode_partition(4, 8, 0, auto, 0) == -1
 
 
+def test_partition_for_lengths(lib):
+    import ctypes as C
+
+    def choose(lens, H):
+        arr = (C.c_int32 * len(lens))(*lens)
+        return lib.pkv_decode_partition_for_lengths(arr if lens else None, len(lens), H)
+
+    def rule(lens, H):  # the header's statement
+        G = -(-H // 4)
+        share = sum(lens) * G // 256
+        if len(lens) * G >= 1024 and max(lens) <= share:
+            return 0
+        size = -(-(share // 2) // 32) * 32
+        if len(lens) * G < 1024:
+            by_shape = lib.pkv_decode_partition(len(lens), H, max(lens), _lib.PKV_PARTITION_AUTO, 0)
+            if 0 < by_shape < size:
+                size = by_shape
+        size = min(2048, max(256 if len(lens) * G < 1024 else 512, size))
+        return 0 if size >= max(lens) else size
+
+    skew = [32768] + [64 + (97 * i) % 1000 for i in range(1, 256)]
+    cases = [(skew, 32), ([4096] + [16] * 255, 32), ([800] * 256, 32), ([4096] * 300, 8),
+             ([4096, 3000, 1, 2049, 700, 4095, 16, 2500], 8), ([1], 1), ([100000, 5], 8), ([2000] * 64, 40)]
+    for lens, H in cases:
+        got = choose(lens, H)
+        assert got == rule(lens, H), (lens[:3], H, got)
+        assert got == 0 or (got % 32 == 0 and 256 <= got <= 2048 and got < max(lens))
+    assert choose(skew, 32) == 2048                  # one long context in a large batch is split
+    assert choose([4096] + [16] * 255, 32) == 512    # which the shape-only rule leaves whole
+    assert lib.pkv_decode_partition(256, 32, 4096, _lib.PKV_PARTITION_AUTO, 0) == 0
+    assert choose([800] * 256, 32) == 0              # an even batch stays whole
+    assert choose([], 8) == 0
+    assert choose([5, 0], 8) == -1 and choose([5], 0) == -1
+    assert lib.pkv_decode_partition_for_lengths(None, 3, 8) == -1
+
+
 def test_bad_arguments_rejected_before_any_launch(lib):
     desc = _lib.CacheDesc(64, 4, 128, 16, _lib.PKV_BF16)
     null = ctypes.c_void_p(0)
