@@ -73,7 +73,8 @@ def _args():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-mixed", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip the sharing and cached-prefix measurements")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="time box of the CPU oracle sample")
+    ap.add_argument("--cpu-seconds", type=float, default=20.0,
+                    help="CPU oracle sample: about a quarter of this per leg (decode / prefill, 1 thread / all cores)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of a known size (for counter calibration) and exit")
     return ap.parse_args()
@@ -120,7 +121,6 @@ def main() -> int:
     from paged_kv_cache_137_amd.blocks import slot_mapping
 
     dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
 
     def up(x, dt=None):
         x = np.ascontiguousarray(x)
@@ -140,6 +140,12 @@ def main() -> int:
 
     # ---------------- decode step (the headline) ----------------
     d = W.decode_config(3, poison=False, with_new_tokens=True)
+    # The CPU oracle baseline runs first: its process pool is forked before this
+    # process initialises the GPU.
+    cpu_line = None
+    if not a.no_cpu_baseline:
+        cpu_line = cpu_baseline(d, W.mixed_prefill(), a.cpu_seconds)
+    torch.cuda.set_device(dev)
     S, H, D = d.q.shape
     sum_ctx = int(d.context_lens.sum())
     kv_bytes = sum_ctx * 2 * H * D * 2
@@ -252,9 +258,8 @@ def main() -> int:
         line["sharing_step"] = sharing_step(a, dev, up)
         line["cached_prefix_prefill"] = cached_prefix_prefill(a, dev, up)
 
-    # ---------------- CPU oracle baseline ----------------
-    if not a.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(d, a.cpu_seconds)
+    if cpu_line is not None:
+        line["cpu_baseline"] = cpu_line
     print(json.dumps(line), flush=True)
     return 0
 
@@ -635,44 +640,149 @@ def swap_step(a, t, n_blocks: int = 2048):
 
 
 def _cpu_model() -> str:
+    """The host CPU as /proc/cpuinfo describes it: model name, family / model /
+    stepping, clock and cache (a virtual machine may report a generic name)."""
+    info = {}
     try:
         for ln in open("/proc/cpuinfo"):
-            if ln.startswith("model name"):
-                return ln.split(":", 1)[1].strip()
+            if ":" in ln:
+                k, v = ln.split(":", 1)
+                info.setdefault(k.strip(), v.strip())
+            elif info:
+                break  # the first processor's block is enough
     except OSError:
-        pass
-    return "unknown"
+        return "unknown"
+    parts = [info.get("model name", "unknown")]
+    ids = [f"{k} {info[k]}" for k in ("cpu family", "model", "stepping") if k in info]
+    if ids:
+        parts.append("(" + ", ".join(ids) + ")")
+    if "cpu MHz" in info:
+        parts.append(f"{float(info['cpu MHz']):.0f} MHz")
+    if "cache size" in info:
+        parts.append(f"cache {info['cache size']}")
+    return " ".join(parts)
 
 
-def cpu_baseline(d, seconds: float):
-    """The float64 oracle on whole sequences of the same step, one thread.
+# The all-core CPU runs use a process pool forked before this process touches
+# the GPU; the workers read these inputs (inherited through fork) and do only
+# NumPy work, one BLAS thread each.
+_CPU_DECODE = None
+_CPU_PREFILL = None
 
-    Sequences are taken in order, wrapping round to the first again, until
-    `seconds` have passed; the rate is K/V bytes attended per second."""
+
+def _cpu_worker_init():
     import threadpoolctl
+
+    global _CPU_LIMIT
+    _CPU_LIMIT = threadpoolctl.threadpool_limits(1)
+
+
+def _cpu_decode_seq(s_):
+    import oracle
+
+    d = _CPU_DECODE
+    oracle.attention.paged_decode(d.q, d.k_cache, d.v_cache, d.block_tables, d.context_lens, d.scale, d.dtype,
+                                  seqs=[s_])
+    return int(d.context_lens[s_])
+
+
+def _prefill_units(p, heads_per_unit=4):
+    return [(i, h0) for i in range(len(p.prompt_lens)) for h0 in range(0, p.num_heads, heads_per_unit)]
+
+
+def _cpu_prefill_unit(unit, p=None):
+    """The oracle's causal prefill of one prompt for 4 of its heads; returns the
+    unit's causal FLOPs (4 * D * heads * L(L+1)/2)."""
+    import numpy as np
 
     import oracle
 
+    p = _CPU_PREFILL if p is None else p
+    i, h0 = unit
+    hs = slice(h0, min(h0 + 4, p.num_heads))
+    off = int(p.prompt_lens[:i].sum())
+    L = int(p.prompt_lens[i])
+    sub = [np.ascontiguousarray(x[off:off + L, hs]) for x in (p.q, p.k, p.v)]
+    oracle.attention.causal_prefill(*sub, [L], 1.0 / np.sqrt(p.head_dim), p.dtype)
+    return 4.0 * p.head_dim * sub[0].shape[1] * L * (L + 1) / 2
+
+
+def cpu_baseline(d, p, seconds: float, max_workers: int = 16):
+    """The float64 oracle, as it stands, on the host cores: one thread, then every
+    core of this process's CPU share (at most max_workers; the box gives one GPU
+    a share of 16).
+
+    Decode: whole sequences of the headline step (the oracle's paged_decode on
+    one sequence), in order, wrapping round.  Prefill: config 5's prompts in
+    units of (prompt, 4 heads), the oracle's causal_prefill on each.  Each leg
+    runs about seconds / 4.  The one-thread legs are time-boxed; the all-core
+    legs map a fixed list of units, sized from the one-thread rate, over a
+    process pool (one BLAS thread per process).  Must run before this process
+    initialises the GPU (the pool is forked)."""
+    import multiprocessing as mp
+
+    import threadpoolctl
+
+    global _CPU_DECODE, _CPU_PREFILL
+    _CPU_DECODE, _CPU_PREFILL = d, p
     H, D = d.num_heads, d.head_dim
-    done, tokens = 0, 0
+    per_tok = 2 * H * D * 2
+    leg = seconds / 4
+    affinity = len(os.sched_getaffinity(0))
+    cores = max(1, min(affinity, max_workers))
+
     with threadpoolctl.threadpool_limits(1):
+        done, tokens = 0, 0
         t0 = time.perf_counter()
-        while (time.perf_counter() - t0) < seconds:
-            s_ = done % d.num_seqs
-            oracle.attention.paged_decode(d.q, d.k_cache, d.v_cache, d.block_tables, d.context_lens, d.scale,
-                                          d.dtype, seqs=[s_])
-            tokens += int(d.context_lens[s_])
+        while time.perf_counter() - t0 < leg:
+            tokens += _cpu_decode_seq(done % d.num_seqs)
             done += 1
-        el = time.perf_counter() - t0
+        dec1 = (done, tokens, time.perf_counter() - t0)
+        units = _prefill_units(p)
+        n1, fl1 = 0, 0.0
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < leg:
+            fl1 += _cpu_prefill_unit(units[(n1 * 7) % len(units)])
+            n1 += 1
+        pre1 = (n1, fl1, time.perf_counter() - t0)
+
+    ctx = mp.get_context("fork")
+    with ctx.Pool(cores, initializer=_cpu_worker_init) as pool:
+        nd = max(cores, min(64 * d.num_seqs, int(dec1[0] / dec1[2] * cores * leg)))
+        t0 = time.perf_counter()
+        tok_all = sum(pool.map(_cpu_decode_seq, [i % d.num_seqs for i in range(nd)], chunksize=1))
+        dec_all = time.perf_counter() - t0
+        npf = max(cores, min(64 * len(units), int(pre1[0] / pre1[2] * cores * leg)))
+        t0 = time.perf_counter()
+        fl_all = sum(pool.map(_cpu_prefill_unit, [units[(i * 7) % len(units)] for i in range(npf)], chunksize=1))
+        pre_all = time.perf_counter() - t0
+    _CPU_DECODE = _CPU_PREFILL = None
+
     return {
-        "value": round(tokens * 2 * H * D * 2 / el / 1e9, 4),
+        "value": round(tok_all * per_tok / dec_all / 1e9, 4),
         "unit": "GB/s",
-        "cores": 1,
+        "cores": cores,
         "kind": "oracle",
-        "tokens_attended_per_s": round(tokens / el, 1),
+        "sample": f"{nd} whole-sequence decodes of the headline step's {d.num_seqs} sequences, in order and "
+                  f"wrapping round ({tok_all} tokens, {dec_all:.1f} s), float64 NumPy, over {cores} processes "
+                  f"with one BLAS thread each",
+        "tokens_attended_per_s": round(tok_all / dec_all, 1),
+        "host_cores_in_affinity": affinity,
         "cpu_model": _cpu_model(),
-        "sample": f"{done} whole-sequence decodes from the same step's {d.num_seqs} sequences, in order and "
-                  f"wrapping round ({tokens} tokens, {el:.1f} s), float64 NumPy, BLAS limited to 1 thread",
+        "one_thread": {
+            "value": round(dec1[1] * per_tok / dec1[2] / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "tokens_attended_per_s": round(dec1[1] / dec1[2], 1),
+            "sample": f"{dec1[0]} whole-sequence decodes ({dec1[1]} tokens, {dec1[2]:.1f} s), BLAS limited to 1 thread",
+        },
+        "prefill": {
+            "workload": "config 5's 8 prompts (32 heads x 128, bf16 inputs), causal, float64 oracle, in units of "
+                        "(prompt, 4 heads)",
+            "all_cores_GFLOPs": round(fl_all / pre_all / 1e9, 3), "all_cores_units": npf,
+            "all_cores_seconds": round(pre_all, 2), "cores": cores,
+            "one_thread_GFLOPs": round(pre1[1] / pre1[2] / 1e9, 3), "one_thread_units": pre1[0],
+            "one_thread_seconds": round(pre1[2], 2),
+            "flops_counted": "causal algorithmic FLOPs, 4 x head_dim x heads x L(L+1)/2 per unit",
+        },
     }
 
 

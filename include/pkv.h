@@ -30,9 +30,11 @@
  *  - Element types: pkv_dtype.  bf16 is the upper half of an IEEE float32.
  *  - Set PKV_VALIDATE=1 in the environment to make each call copy its index
  *    arrays to the host and check them before launching: table entries in
- *    range, context lengths in [1, max_context_len], slots unique and in range.
- *    This mode synchronises the stream; it is for tests.  A failed check
- *    returns PKV_EINVAL.
+ *    range, context lengths in [1, max_context_len], slots unique and in range,
+ *    copy destinations distinct and not also sources, prompt lengths in range
+ *    and summing to total_tokens.  The variable is read at every call.  This
+ *    mode synchronises the stream; it is for tests.  A failed check returns
+ *    PKV_EINVAL and launches nothing.
  *  - PKV_DECODE_WG_PER_CU (1 to 16, default 1) sets how many workgroups per CU
  *    the per-sequence decode keeps resident; it is read at every launch and
  *    exists to measure other launch shapes.  Results do not depend on it.
@@ -134,31 +136,37 @@ size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t h
                                   int32_t max_context_len, int32_t partition_size);
 
 /*
- * The partition size a decode call uses for these arguments: partition_size
- * itself, or what PKV_PARTITION_AUTO resolves to (0 = no split) for the plain
- * decode (shared == 0) or the shared-prefix decode (shared != 0), which follow
- * the same rule; see pkv_paged_attn_decode.  Host arithmetic only.  Returns -1 for an invalid
- * shape (num_seqs < 0, num_heads <= 0 or max_context_len <= 0).  The value is
+ * The partition size a decode call uses for these arguments, written to
+ * *partition_out: partition_size itself, or what PKV_PARTITION_AUTO resolves to
+ * (0 = no split) for the plain decode (shared == 0) or the shared-prefix
+ * decode (shared != 0), which follow the same rule; see pkv_paged_attn_decode.
+ * Host arithmetic only.  Returns PKV_OK, or PKV_EINVAL (and leaves
+ * *partition_out alone) for a null partition_out, num_seqs < 0, num_heads <= 0,
+ * max_context_len <= 0 or partition_size < PKV_PARTITION_AUTO.  The value is
  * not checked against the block size: the decode call does that.
  */
-int32_t pkv_decode_partition(int32_t num_seqs, int32_t num_heads, int32_t max_context_len, int32_t partition_size,
-                             int32_t shared);
+int pkv_decode_partition(int32_t num_seqs, int32_t num_heads, int32_t max_context_len, int32_t partition_size,
+                         int32_t shared, int32_t* partition_out);
 
 /*
  * A partition size for pkv_paged_attn_decode (and the shared-prefix decode)
  * chosen from the context lengths themselves, for callers that hold them on
- * the host (a scheduler does).  context_lens: HOST int32 [num_seqs], each >= 1.
- * With G = ceil(num_heads / 4) head groups and share = sum(context_lens) * G /
- * 256 (one CU's part of the batch): 0 (no split) when num_seqs * G >= 1024 and
- * the longest context is at most share; otherwise about share / 2 rounded up to
- * a multiple of 32, no larger than what PKV_PARTITION_AUTO gives a batch of
- * fewer than 1024 units, between 512 (256 for fewer than 1024 units) and 2048
- * tokens, and 0 if that covers the longest context.  Unlike PKV_PARTITION_AUTO it splits a large batch of nearly
- * empty contexts beside one long one.  Pass the result as partition_size, to
- * the workspace sizing call as well.  Host arithmetic only; returns -1 for
- * num_seqs < 0, num_heads <= 0, a null pointer or a length below 1.
+ * the host (a scheduler does), written to *partition_out.  context_lens: HOST
+ * int32 [num_seqs], each >= 1.  With G = ceil(num_heads / 4) head groups and
+ * share = sum(context_lens) * G / 256 (one CU's part of the batch): 0 (no
+ * split) when num_seqs * G >= 1024 and the longest context is at most share;
+ * otherwise about share / 2 rounded up to a multiple of 32, no larger than
+ * what PKV_PARTITION_AUTO gives a batch of fewer than 1024 units, between 512
+ * (256 for fewer than 1024 units) and 2048 tokens, and 0 if that covers the
+ * longest context.  Unlike PKV_PARTITION_AUTO it splits a large batch of
+ * nearly empty contexts beside one long one.  Pass the result as
+ * partition_size, to the workspace sizing call as well.  Host arithmetic only.
+ * Returns PKV_OK, or PKV_EINVAL (and leaves *partition_out alone) for a null
+ * pointer, num_seqs < 0, num_heads <= 0 or a length below 1: an invalid batch
+ * never turns into a partition size.
  */
-int32_t pkv_decode_partition_for_lengths(const int32_t* context_lens, int32_t num_seqs, int32_t num_heads);
+int pkv_decode_partition_for_lengths(const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                                     int32_t* partition_out);
 
 /*
  * pkv_paged_attn_decode - attention of each sequence's current token over its
@@ -178,7 +186,9 @@ int32_t pkv_decode_partition_for_lengths(const int32_t* context_lens, int32_t nu
  *   k_cache, v_cache  the pool (read only)
  *   block_tables  int32 [num_seqs][max_blocks_per_seq] physical ids
  *   context_lens  int32 [num_seqs], each in [1, max_context_len];
- *                 max_context_len <= max_blocks_per_seq * block_size
+ *                 max_context_len <= max_blocks_per_seq * block_size.  The
+ *                 softmax over an empty context is undefined: a sequence with
+ *                 context length 0 gets NaN in every output element.
  *   scale         multiplies q.k before the softmax (usually 1/sqrt(head_dim))
  *   out           [num_seqs][num_heads][head_dim] of out_dtype (PKV_F32 or desc->dtype)
  *   partition_size  tokens per context partition: a multiple of the block size,

@@ -26,8 +26,8 @@ SIGNATURES = {
     "pkv_check_device": ([], ctypes.c_int),
     "pkv_kv_cache_write": ([_vp, _vp, _vp, _i64, _vp, _vp, _vp, _vp], ctypes.c_int),
     "pkv_decode_workspace_bytes": ([_i32, _i32, _i32, _i32, _i32], _sz),
-    "pkv_decode_partition": ([_i32, _i32, _i32, _i32, _i32], _i32),
-    "pkv_decode_partition_for_lengths": ([_vp, _i32, _i32], _i32),
+    "pkv_decode_partition": ([_i32, _i32, _i32, _i32, _i32, _vp], ctypes.c_int),
+    "pkv_decode_partition_for_lengths": ([_vp, _i32, _i32, _vp], ctypes.c_int),
     "pkv_paged_attn_decode": (_DECODE_ARGS, ctypes.c_int),
     "pkv_paged_attn_decode_partial": (_DECODE_ARGS, ctypes.c_int),
     "pkv_paged_attn_decode_reduce": (_DECODE_ARGS, ctypes.c_int),

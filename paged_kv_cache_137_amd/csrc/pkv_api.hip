@@ -14,7 +14,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 1;
+constexpr int kAbiVersion = 2;
 constexpr int kBlock = 16;
 constexpr int kMaxDevices = 64;
 int g_arch[kMaxDevices];  // 0 = not yet checked, 1 = gfx950, -1 = other
@@ -22,12 +22,10 @@ int g_arch[kMaxDevices];  // 0 = not yet checked, 1 = gfx950, -1 = other
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 bool valid_dtype(int d) { return d == PKV_F32 || d == PKV_F16 || d == PKV_BF16; }
 
+// PKV_VALIDATE is read at every call, so a process (a test) can switch it.
 bool validate_mode() {
-  static const bool on = [] {
-    const char* e = std::getenv("PKV_VALIDATE");
-    return e != nullptr && e[0] != '\0' && e[0] != '0';
-  }();
-  return on;
+  const char* e = std::getenv("PKV_VALIDATE");
+  return e != nullptr && e[0] != '\0' && e[0] != '0';
 }
 
 int device_status() {
@@ -303,21 +301,28 @@ size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t h
   return plan_decode(num_seqs, num_heads, head_dim, max_context_len, partition_size).ws_bytes;
 }
 
-int32_t pkv_decode_partition(int32_t num_seqs, int32_t num_heads, int32_t max_context_len, int32_t partition_size,
-                             int32_t shared) {
-  if (num_seqs < 0 || num_heads <= 0 || max_context_len <= 0) return -1;
-  return resolve_partition(partition_size, num_seqs, num_heads, max_context_len, shared != 0);
+int pkv_decode_partition(int32_t num_seqs, int32_t num_heads, int32_t max_context_len, int32_t partition_size,
+                         int32_t shared, int32_t* partition_out) {
+  if (partition_out == nullptr || num_seqs < 0 || num_heads <= 0 || max_context_len <= 0) return PKV_EINVAL;
+  if (partition_size < PKV_PARTITION_AUTO) return PKV_EINVAL;
+  *partition_out = resolve_partition(partition_size, num_seqs, num_heads, max_context_len, shared != 0);
+  return PKV_OK;
 }
 
-int32_t pkv_decode_partition_for_lengths(const int32_t* context_lens, int32_t num_seqs, int32_t num_heads) {
-  if (num_seqs < 0 || num_heads <= 0 || (num_seqs > 0 && context_lens == nullptr)) return -1;
+int pkv_decode_partition_for_lengths(const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                                     int32_t* partition_out) {
+  if (partition_out == nullptr || num_seqs < 0 || num_heads <= 0 || (num_seqs > 0 && context_lens == nullptr))
+    return PKV_EINVAL;
   int64_t total = 0, longest = 0;
   for (int32_t s = 0; s < num_seqs; ++s) {
-    if (context_lens[s] < 1) return -1;
+    if (context_lens[s] < 1) return PKV_EINVAL;
     total += context_lens[s];
     longest = context_lens[s] > longest ? context_lens[s] : longest;
   }
-  if (num_seqs == 0) return 0;
+  if (num_seqs == 0) {
+    *partition_out = 0;
+    return PKV_OK;
+  }
   // Each unit covers kAutoHeadsPerUnit heads of one partition; with G head
   // groups a CU's share of the batch is total * G / 256 unit-tokens.  Contexts
   // stay whole when the batch has the units and its longest context is at most
@@ -326,7 +331,10 @@ int32_t pkv_decode_partition_for_lengths(const int32_t* context_lens, int32_t nu
   // below that, partial results and merges cost more than the balance gains.
   const int64_t groups = (num_heads + kAutoHeadsPerUnit - 1) / kAutoHeadsPerUnit;
   const int64_t share = total * groups / 256;
-  if ((int64_t)num_seqs * groups >= kAutoTargetUnits && longest <= share) return 0;
+  if ((int64_t)num_seqs * groups >= kAutoTargetUnits && longest <= share) {
+    *partition_out = 0;
+    return PKV_OK;
+  }
   int64_t size = (share / 2 + 31) / 32 * 32;
   if (num_seqs * groups < kAutoTargetUnits) {  // few units: as many as the shape rule makes, at least
     const int32_t by_shape = resolve_partition(PKV_PARTITION_AUTO, num_seqs, num_heads, (int32_t)longest, false);
@@ -335,7 +343,8 @@ int32_t pkv_decode_partition_for_lengths(const int32_t* context_lens, int32_t nu
   const int64_t floor = num_seqs * groups < kAutoTargetUnits ? 256 : 512;
   if (size < floor) size = floor;
   if (size > kAutoMaxPartition) size = kAutoMaxPartition;
-  return size >= longest ? 0 : (int32_t)size;
+  *partition_out = size >= longest ? 0 : (int32_t)size;
+  return PKV_OK;
 }
 
 size_t pkv_decode_shared_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim,

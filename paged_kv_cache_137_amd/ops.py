@@ -105,20 +105,35 @@ def decode_shared_workspace_bytes(num_seqs: int, num_heads: int, head_dim: int, 
 
 def decode_partition(num_seqs: int, num_heads: int, max_context_len: int,
                      partition_size: int = DEFAULT_PARTITION, shared: bool = False) -> int:
-    """The partition size (0 = no split) a decode call uses for these arguments."""
-    return int(lib().pkv_decode_partition(num_seqs, num_heads, max_context_len, partition_size, int(shared)))
+    """The partition size (0 = no split) a decode call uses for these arguments.
+
+    Raises ValueError for an invalid shape (num_seqs < 0, num_heads <= 0,
+    max_context_len <= 0, partition_size below PARTITION_AUTO)."""
+    res = ctypes.c_int32(0)
+    st = lib().pkv_decode_partition(num_seqs, num_heads, max_context_len, partition_size, int(shared),
+                                    ctypes.byref(res))
+    if st != _lib.PKV_OK:
+        raise ValueError(f"decode_partition: invalid shape ({lib().pkv_status_str(st).decode()})")
+    return int(res.value)
 
 
 def decode_partition_for_lengths(context_lens, num_heads: int) -> int:
     """A partition size chosen from the context lengths themselves (host values:
-    a sequence of ints or a CPU array), for callers that know them; 0 = no split."""
+    a sequence of ints or a CPU array), for callers that know them; 0 = no split.
+
+    Raises ValueError when a length is below 1 or num_heads <= 0: an invalid
+    batch never becomes a partition size (in particular not PARTITION_AUTO)."""
     import numpy as np
 
     lens = np.ascontiguousarray(np.asarray(context_lens, dtype=np.int32))
     if lens.ndim != 1:
         raise ValueError("context_lens must be one-dimensional")
-    return int(lib().pkv_decode_partition_for_lengths(lens.ctypes.data if lens.size else None, int(lens.size),
-                                                      int(num_heads)))
+    res = ctypes.c_int32(0)
+    st = lib().pkv_decode_partition_for_lengths(lens.ctypes.data if lens.size else None, int(lens.size),
+                                                int(num_heads), ctypes.byref(res))
+    if st != _lib.PKV_OK:
+        raise ValueError(f"decode_partition_for_lengths: invalid batch ({lib().pkv_status_str(st).decode()})")
+    return int(res.value)
 
 
 def _decode_call(fn_name, q, k_cache, v_cache, block_tables, context_lens, scale, out,
@@ -166,10 +181,13 @@ def paged_attn_decode(q, k_cache, v_cache, block_tables, context_lens, scale, ou
     max_context_len bounds every context_lens entry.  By default it is the table
     capacity (max_blocks_per_seq * block_size).  partition_size = 0 disables the
     split-context path; PARTITION_AUTO (the default) lets the library choose from
-    the batch shape: no split when num_seqs * ceil(num_heads / 4) >= 1024 and no
-    context exceeds 4096 tokens, else partitions of 256 to 2048 tokens that give
-    about that many units (decode_partition reports the choice).  Without a
-    workspace, one is allocated through torch.
+    the batch shape: no split when num_seqs * ceil(num_heads / 4) >= 1024 and
+    max_context_len is at most 4096 tokens, else partitions of 256 to 2048 tokens
+    that give about that many units (decode_partition reports the choice).  The
+    rule reads max_context_len, not the lengths on the device: with the default
+    (the table capacity), tables padded past 4096 tokens make a large batch
+    split even when every real context is short; pass the real maximum when it
+    is known.  Without a workspace, one is allocated through torch.
     """
     return _decode_call("pkv_paged_attn_decode", q, k_cache, v_cache, block_tables, context_lens, scale, out,
                         max_context_len, partition_size, workspace)

@@ -416,6 +416,16 @@ def sharing_config(*, groups: int = 128, samples: int = 4, poison: bool = True,
     )
 
 
+def mixed_prefill(*, seed: int | None = None, num_prompts: int = 8, prompt_range=(128, 2048), heads: int = 32,
+                  head_dim: int = 128, dtype: str = "bf16") -> PrefillInputs:
+    """The prompts of config 5 alone: the same lengths and values as
+    mixed_config's prefill, without drawing the decode pool."""
+    seed = config_seed(5) if seed is None else seed
+    lr = np.random.default_rng([seed, 0])
+    Lp = lr.integers(prompt_range[0], prompt_range[1] + 1, size=num_prompts).astype(np.int32)
+    return make_prefill(seed, dtype, heads, head_dim, Lp)
+
+
 def mixed_config(*, poison: bool = True, seed: int | None = None, num_prompts: int = 8,
                  num_decodes: int = 192, prompt_range=(128, 2048), heads: int = 32,
                  head_dim: int = 128, dtype: str = "bf16") -> MixedInputs:

@@ -49,24 +49,25 @@ def upload_decode(d, dev="cuda"):
     )
 
 
-def run_decode(ops, t, d, out_dtype="f32", partition_size=512, fn=None):
-    out = torch.empty(d.q.shape, dtype=TORCH_DT[out_dtype], device=t["q"].device)
+def run_decode(ops, t, d, out_dtype="f32", partition_size=512, fn=None, fill=float("nan")):
+    out = nan_out(d.q.shape, out_dtype, dev=t["q"].device, fill=fill)
     (fn or ops.paged_attn_decode)(t["q"], t["k_cache"], t["v_cache"], t["block_tables"], t["context_lens"],
                                   d.scale, out, max_context_len=d.max_context_len, partition_size=partition_size)
     return out
 
 
-def sample_seqs(context_lens: np.ndarray, k: int, seed: int = 0) -> list[int]:
-    """A spread of sequences: shortest, longest, every partition-count class, plus random ones."""
-    n = len(context_lens)
-    if n <= k:
-        return list(range(n))
-    order = np.argsort(context_lens, kind="stable")
-    picks = {int(order[0]), int(order[-1])}
-    parts = (context_lens + 511) // 512
-    for pc in np.unique(parts):
-        picks.add(int(np.nonzero(parts == pc)[0][0]))
-    rng = np.random.default_rng(seed)
-    rest = [i for i in rng.permutation(n) if int(i) not in picks]
-    picks.update(int(i) for i in rest[: max(0, k - len(picks))])
-    return sorted(picks)
+def nan_out(shape, out_dtype: str | torch.dtype = "f32", dev="cuda", fill=float("nan")) -> torch.Tensor:
+    """An output buffer filled with NaN before the launch, so that any element a
+    kernel fails to write fails the comparison instead of passing on stale data.
+    Tests that expect NaN outputs pass a finite `fill` instead."""
+    dt = TORCH_DT[out_dtype] if isinstance(out_dtype, str) else out_dtype
+    return torch.full(tuple(shape), fill, dtype=dt, device=dev)
+
+
+def timed(fn, *args, **kw):
+    """(fn(*args, **kw), seconds it took)."""
+    import time
+
+    t0 = time.perf_counter()
+    r = fn(*args, **kw)
+    return r, time.perf_counter() - t0

@@ -17,74 +17,101 @@ import oracle
 from paged_kv_cache_137_amd import ops
 from paged_kv_cache_137_amd import workloads as W
 from paged_kv_cache_137_amd.blocks import slot_mapping
-from _dev import TOL, bits, down, rne_to, run_decode, sample_seqs, up, upload_decode
+import _refs as refs
+from _dev import TOL, bits, down, nan_out, rne_to, run_decode, timed, up, upload_decode
+from _records import record
 
 pytestmark = pytest.mark.gpu
 
 
-def _check(d, out32, outdt, seqs, kc=None, vc=None):
-    ref = oracle.attention.paged_decode(d.q, d.k_cache if kc is None else kc, d.v_cache if vc is None else vc,
-                                        d.block_tables, d.context_lens, d.scale, d.dtype, seqs=seqs)
+def _check(d, out32, outdt, seqs=None, kc=None, vc=None, ref=None):
+    """Compare the f32 output with the oracle on `seqs` (default: every sequence);
+    a 16-bit output must be the nearest-even rounding of the f32 one.  Returns
+    (max|err|, oracle seconds)."""
+    seqs = list(range(d.num_seqs)) if seqs is None else seqs
+    t_or = 0.0
+    if ref is None:
+        ref, t_or = timed(oracle.attention.paged_decode, d.q, d.k_cache if kc is None else kc,
+                          d.v_cache if vc is None else vc, d.block_tables, d.context_lens, d.scale, d.dtype,
+                          block_size=d.block_size, seqs=seqs)
     got = down(out32)
-    assert np.isfinite(got).all()
+    assert np.isfinite(got).all(), "an output the kernel should have written is still NaN"
     err = float(np.abs(got[seqs] - ref[seqs]).max())
-    print(f"  {d.dtype} seqs={len(seqs)} max|err|={err:.3e}", flush=True)
+    print(f"  {d.dtype} seqs={len(seqs)} max|err|={err:.3e} oracle {t_or:.1f} s", flush=True)
     assert err <= TOL[d.dtype]
     if outdt is not None:
         assert np.array_equal(bits(down(outdt)), bits(rne_to(got, d.dtype)))
-    return err
+    return err, t_or
 
 
 @pytest.mark.parametrize("cfg", [1, 2, 4])
 def test_decode_config_parity(cfg):
+    """Configs 1, 2 and 4 at full size, every sequence and head against the oracle."""
     print(f"decode parity config {cfg}", flush=True)
     d = W.decode_config(cfg)
     t = upload_decode(d)
-    out32 = run_decode(ops, t, d, "f32")
-    outdt = None if d.dtype == "f32" else run_decode(ops, t, d, d.dtype)
-    seqs = list(range(d.num_seqs)) if cfg in (1, 2) else sample_seqs(d.context_lens, 48)
-    _check(d, out32, outdt, seqs)
+    out32 = run_decode(ops, t, d, "f32", partition_size=ops.PARTITION_AUTO)
+    outdt = None if d.dtype == "f32" else run_decode(ops, t, d, d.dtype, partition_size=ops.PARTITION_AUTO)
+    ref, t_or = refs.decode_ref(cfg, d)
+    err, _ = _check(d, out32, outdt, ref=ref)
+    record(f"config{cfg}", "paged_attn_decode (automatic partition)", max_abs_err=err, tol=TOL[d.dtype],
+           sequences=d.num_seqs, heads=d.num_heads, outputs_compared=int(out32.numel()),
+           bit_exact_16bit_output_is_rne_of_f32=outdt is not None, oracle_seconds=round(t_or, 2),
+           partition=ops.decode_partition(d.num_seqs, d.num_heads, d.max_context_len))
     if cfg == 1:  # the ceil(len/16) block counts of the tiny config (300 tokens -> 19 blocks)
         assert d.block_tables.shape[1] == 19
 
 
 def test_decode_config3_bench_launch():
-    """Config 3 at full size: write the 256 current tokens, then partitions of
-    512 plus the reduce, and the launch the benchmark times (the automatic
-    partition, which for 256 sequences x 8 head groups is no split)."""
+    """Config 3 at full size, every sequence: write the 256 current tokens, then
+    partitions of 512 plus the reduce (the configuration as written), and the
+    launch the benchmark times (the automatic partition, which for 256
+    sequences x 8 head groups is no split)."""
     print("decode parity config 3 (write + partial + reduce)", flush=True)
     d = W.decode_config(3, with_new_tokens=True)
     t = upload_decode(d)
     sm = slot_mapping(d.block_tables, range(d.num_seqs), d.context_lens - 1)
     ops.kv_cache_write(up(d.k_new, d.dtype), up(d.v_new, d.dtype), up(sm), t["k_cache"], t["v_cache"])
-    out32 = torch.empty(d.q.shape, dtype=torch.float32, device="cuda")
+    kc, vc = oracle.attention.cache_write(d.k_cache, d.v_cache, d.k_new, d.v_new, sm, 16)
+    write_exact = np.array_equal(bits(down(t["k_cache"])), bits(kc)) and np.array_equal(bits(down(t["v_cache"])),
+                                                                                           bits(vc))
+    assert write_exact
+    out32 = nan_out(d.q.shape)
     ws = torch.empty(ops.decode_workspace_bytes(d.num_seqs, 32, 128, d.max_context_len, 512), dtype=torch.uint8,
                      device="cuda")
     args = (t["q"], t["k_cache"], t["v_cache"], t["block_tables"], t["context_lens"], d.scale, out32)
     kw = dict(max_context_len=d.max_context_len, partition_size=512, workspace=ws)
     ops.paged_attn_decode_partial(*args, **kw)
     ops.paged_attn_decode_reduce(*args, **kw)
-    outdt = torch.empty(d.q.shape, dtype=torch.bfloat16, device="cuda")
+    outdt = nan_out(d.q.shape, "bf16")
     ops.paged_attn_decode(*args[:-1], outdt, **kw)
-    seqs = sample_seqs(d.context_lens, 40)
-    kc, vc = oracle.attention.cache_write(d.k_cache, d.v_cache, d.k_new, d.v_new, sm, 16)
-    _check(d, out32, outdt, seqs, kc, vc)
+    ref, t_or = timed(oracle.attention.paged_decode, d.q, kc, vc, d.block_tables, d.context_lens, d.scale, d.dtype)
+    err, _ = _check(d, out32, outdt, ref=ref)
     # the stages together are the whole call, bit for bit
-    whole = torch.empty_like(out32)
+    whole = nan_out(d.q.shape)
     ops.paged_attn_decode(*args[:-1], whole, **kw)
     assert torch.equal(whole, out32)
     assert (d.context_lens > 512).sum() > 0
+    record("config3", "kv_cache_write", max_abs_err=0.0, bit_exact_whole_pool=write_exact, tokens=d.num_seqs,
+           oracle_seconds=None)
+    record("config3", "paged_attn_decode partial + reduce (512-token partitions)", max_abs_err=err,
+           tol=TOL[d.dtype], sequences=d.num_seqs, heads=d.num_heads, outputs_compared=int(out32.numel()),
+           bit_exact_16bit_output_is_rne_of_f32=True, bit_exact_partial_plus_reduce_is_whole_call=True,
+           oracle_seconds=round(t_or, 2))
     # the benchmark's launch: automatic partition (no split here), partial then
     # reduce (a no-op without a split)
     assert ops.decode_partition(d.num_seqs, 32, d.max_context_len) == 0
-    auto = torch.empty_like(out32)
+    auto = nan_out(d.q.shape)
     akw = dict(max_context_len=d.max_context_len, partition_size=ops.PARTITION_AUTO)
     ops.paged_attn_decode_partial(*args[:-1], auto, **akw)
     ops.paged_attn_decode_reduce(*args[:-1], auto, **akw)
-    _check(d, auto, None, seqs, kc, vc)
-    nosplit = torch.empty_like(out32)
+    aerr, _ = _check(d, auto, None, ref=ref)
+    nosplit = nan_out(d.q.shape)
     ops.paged_attn_decode(*args[:-1], nosplit, max_context_len=d.max_context_len, partition_size=0)
     assert torch.equal(auto, nosplit)
+    record("config3", "paged_attn_decode (automatic partition: no split; the benchmark's launch)",
+           max_abs_err=aerr, tol=TOL[d.dtype], sequences=d.num_seqs, heads=d.num_heads,
+           outputs_compared=int(auto.numel()), bit_exact_equals_partition_0=True, oracle_seconds=round(t_or, 2))
 
 
 @pytest.mark.parametrize("dt", ["bf16", "f16"])
@@ -114,7 +141,7 @@ def test_decode_auto_partition_bounds_long_contexts():
     assert ops.decode_partition(d.num_seqs, 16, 4096) == 0  # the same batch with contexts <= 4096: no split
     t = upload_decode(d)
     auto = run_decode(ops, t, d, "f32", partition_size=ops.PARTITION_AUTO)
-    _check(d, auto, None, [0, 1, 2, 100, 255])
+    _check(d, auto, None)
     assert torch.equal(auto, run_decode(ops, t, d, "f32", partition_size=2048))
 
 
@@ -158,7 +185,7 @@ def test_decode_many_partitions_plan_batches():
     t = upload_decode(d)
     out32 = run_decode(ops, t, d, "f32", partition_size=256)
     _check(d, out32, None, list(range(d.num_seqs)))
-    shared = torch.empty_like(out32)
+    shared = nan_out(out32.shape, out32.dtype)
     ops.paged_attn_decode_shared(t["q"], t["k_cache"], t["v_cache"], t["block_tables"], t["context_lens"], d.scale,
                                  shared, max_context_len=d.max_context_len, partition_size=256)
     assert torch.equal(shared, out32)
@@ -184,7 +211,7 @@ def test_decode_is_deterministic_and_stages_compose():
     a = run_decode(ops, t, d, "f32")
     b = run_decode(ops, t, d, "f32")
     assert torch.equal(a, b)
-    c = torch.empty_like(a)
+    c = nan_out(a.shape, a.dtype)
     kw = dict(max_context_len=d.max_context_len, partition_size=512)
     args = (t["q"], t["k_cache"], t["v_cache"], t["block_tables"], t["context_lens"], d.scale, c)
     # the reduce reads what the partial stage left in the workspace: one explicit workspace for both
@@ -277,7 +304,7 @@ def test_bad_table_entry_poisons_only_its_sequence():
     d = _batch(51, "bf16", [40, 700, 90], H=4)
     d.block_tables[1, 5] = d.num_blocks + 1000  # outside the pool
     t = upload_decode(d)
-    out = down(run_decode(ops, t, d, "f32"))
+    out = down(run_decode(ops, t, d, "f32", fill=7.0))  # a finite fill: the NaN must come from the kernel
     assert np.isnan(out[1]).all()
     assert np.isfinite(out[[0, 2]]).all()
     ref = oracle.attention.paged_decode(d.q, d.k_cache, d.v_cache, d.block_tables, d.context_lens, d.scale, "bf16",
