@@ -244,6 +244,32 @@ int pkv_paged_attn_decode_reduce(const void* q, const void* k_cache, const void*
                                  int32_t partition_size, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * pkv_paged_attn_decode_noalloc - pkv_paged_attn_decode without a workspace
+ * argument, for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation.
+ *
+ * Arguments, preconditions, result (bit for bit) and errors are those of
+ * pkv_paged_attn_decode with the same partition_size.  The workspace is a
+ * fixed device array inside the library, PKV_NOALLOC_SCRATCH_BYTES per GPU,
+ * which each GPU the library runs on holds until the process ends.  A call
+ * whose workspace (pkv_decode_workspace_bytes for the same arguments) would
+ * exceed it returns PKV_EWORKSPACE and launches nothing; use
+ * pkv_paged_attn_decode with a caller-owned workspace instead.  The call itself
+ * allocates nothing: no hipMalloc, no hipFree, no allocating library routine.
+ * All calls on one GPU share that GPU's array, whose contents a call rebuilds
+ * before use, so calls that can overlap on one GPU (different streams, or
+ * different host threads on one stream without ordering) race and must not be
+ * issued; calls ordered on one stream are safe.  The array's device address is
+ * looked up once per GPU, at the first call made with that GPU current
+ * (PKV_EDEVICE if the lookup fails).
+ */
+#define PKV_NOALLOC_SCRATCH_BYTES (64u << 20)
+int pkv_paged_attn_decode_noalloc(const void* q, const void* k_cache, const void* v_cache, const pkv_cache_desc* desc,
+                                  const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                  int32_t num_seqs, int32_t max_context_len, float scale, void* out,
+                                  int32_t out_dtype, int32_t partition_size, void* stream);
+
+/*
  * pkv_paged_attn_decode_shared - pkv_paged_attn_decode for batches whose
  * sequences share leading blocks: parallel samples of one request, or
  * requests with a common prefix, whose tables hold the same physical ids for

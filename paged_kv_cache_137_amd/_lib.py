@@ -16,6 +16,7 @@ LIB_PATH = os.path.join(HERE, "libpkv.so")
 PKV_F32, PKV_F16, PKV_BF16 = 0, 1, 2
 PKV_PARTITION_AUTO = -1  # the library picks the decode's context partition
 PKV_OK, PKV_EINVAL, PKV_ENOTSUP, PKV_ELAUNCH, PKV_EDEVICE, PKV_EWORKSPACE = 0, -1, -2, -3, -4, -5
+PKV_NOALLOC_SCRATCH_BYTES = 64 << 20  # the device scratch of pkv_paged_attn_decode_noalloc, per GPU
 
 # Every function include/pkv.h declares, with its ctypes signature.
 _i32, _i64, _sz, _vp, _f32 = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_float
@@ -33,6 +34,8 @@ SIGNATURES = {
     "pkv_paged_attn_decode_reduce": (_DECODE_ARGS, ctypes.c_int),
     "pkv_decode_shared_workspace_bytes": ([_i32, _i32, _i32, _i32, _i32], _sz),
     "pkv_paged_attn_decode_shared": (_DECODE_ARGS, ctypes.c_int),
+    "pkv_paged_attn_decode_noalloc": ([_vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _f32, _vp, _i32, _i32, _vp],
+                                      ctypes.c_int),
     "pkv_copy_blocks": ([_vp, _vp, _vp, _vp, _i64, _vp], ctypes.c_int),
     "pkv_swap_blocks": ([_vp, _vp, _i64, _vp, _vp, _i64, _vp, _vp, _i64, _vp], ctypes.c_int),
     "pkv_paged_attn_prefill_cached": (

@@ -7,6 +7,7 @@
 #include <algorithm>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "pkv.h"
@@ -233,6 +234,33 @@ int decode_impl(int stages, bool shared, const void* q, const void* k_cache, con
   return PKV_OK;
 }
 
+// Device scratch of pkv_paged_attn_decode_noalloc: the decode workspace for
+// callers that cannot allocate.  Every GPU the library runs on holds its own
+// copy of this array until the process ends.  In host code `scratch` names a
+// host-side stand-in, not a device address: host code uses only the address
+// hipGetSymbolAddress reports for the current device (scratch_ptr below).
+static __device__ __align__(256) unsigned char scratch[PKV_NOALLOC_SCRATCH_BYTES];
+
+// The device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept; nullptr if the lookup fails.
+void* scratch_ptr(int dev) {
+  static std::mutex mu;
+  static void* ptrs[kMaxDevices];
+  static bool done[kMaxDevices];
+  if (dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!done[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) {
+      (void)hipGetLastError();  // clear the failed query's error state
+      return nullptr;           // not cached: a later call may retry
+    }
+    ptrs[dev] = p;
+    done[dev] = true;
+  }
+  return ptrs[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -371,6 +399,28 @@ int pkv_paged_attn_decode(const void* q, const void* k_cache, const void* v_cach
                           int32_t partition_size, void* workspace, size_t workspace_bytes, void* stream) {
   return decode_impl(kBoth, false, q, k_cache, v_cache, desc, block_tables, max_blocks_per_seq, context_lens, num_seqs,
                      max_context_len, scale, out, out_dtype, partition_size, workspace, workspace_bytes, stream);
+}
+
+int pkv_paged_attn_decode_noalloc(const void* q, const void* k_cache, const void* v_cache, const pkv_cache_desc* desc,
+                                  const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                  int32_t num_seqs, int32_t max_context_len, float scale, void* out,
+                                  int32_t out_dtype, int32_t partition_size, void* stream) {
+  int st = check_desc(desc);
+  if (st != PKV_OK) return st;
+  if (num_seqs < 0 || max_context_len <= 0 || partition_size < PKV_PARTITION_AUTO) return PKV_EINVAL;
+  if (num_seqs == 0) return PKV_OK;
+  const int32_t part = resolve_partition(partition_size, num_seqs, desc->num_heads, max_context_len, false);
+  const size_t need = plan_decode(num_seqs, desc->num_heads, desc->head_dim, max_context_len, part,
+                                  desc->block_size).ws_bytes;
+  if (need > (size_t)PKV_NOALLOC_SCRATCH_BYTES) return PKV_EWORKSPACE;
+  st = device_status();
+  if (st != PKV_OK) return st;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return PKV_EDEVICE;
+  void* ws = scratch_ptr(dev);
+  if (ws == nullptr) return PKV_EDEVICE;
+  return decode_impl(kBoth, false, q, k_cache, v_cache, desc, block_tables, max_blocks_per_seq, context_lens,
+                     num_seqs, max_context_len, scale, out, out_dtype, part, ws, PKV_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 int pkv_paged_attn_decode_partial(const void* q, const void* k_cache, const void* v_cache,

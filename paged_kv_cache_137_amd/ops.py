@@ -193,6 +193,41 @@ def paged_attn_decode(q, k_cache, v_cache, block_tables, context_lens, scale, ou
                         max_context_len, partition_size, workspace)
 
 
+def paged_attn_decode_noalloc(q, k_cache, v_cache, block_tables, context_lens, scale, out, *,
+                              max_context_len: int | None = None, partition_size: int = DEFAULT_PARTITION):
+    """paged_attn_decode without a workspace, for callers that cannot allocate
+    (graph capture, tight serving loops): the library's fixed per-GPU scratch
+    (PKV_NOALLOC_SCRATCH_BYTES) serves instead, and nothing is allocated.  Calls
+    that may overlap on one GPU race on that scratch.  Raises PKVError with
+    PKV_EWORKSPACE when the batch needs more scratch than that."""
+    _need(k_cache, "k_cache", dim=4)
+    dev = k_cache.device
+    _need(v_cache, "v_cache", dtype=k_cache.dtype, device=dev)
+    _need(q, "q", dtype=k_cache.dtype, dim=3, device=dev)
+    _need(block_tables, "block_tables", dtype=torch.int32, dim=2, device=dev)
+    _need(context_lens, "context_lens", dtype=torch.int32, dim=1, device=dev)
+    _need(out, "out", dim=3, device=dev)
+    S, H, D = q.shape
+    if v_cache.shape != k_cache.shape or (H, D) != (k_cache.shape[1], k_cache.shape[3]):
+        raise ValueError("q [S][H][D] does not match the cache")
+    if out.shape != q.shape or out.dtype not in (torch.float32, q.dtype):
+        raise ValueError("out must be [S][H][D] of float32 or q's dtype")
+    if block_tables.shape[0] != S or context_lens.shape[0] != S:
+        raise ValueError("block_tables/context_lens must have one row per sequence")
+    mbps = block_tables.shape[1]
+    if max_context_len is None:
+        max_context_len = mbps * k_cache.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    desc = cache_desc(k_cache)
+    with torch.cuda.device(dev):
+        check("pkv_paged_attn_decode_noalloc", lib().pkv_paged_attn_decode_noalloc(
+            _ptr(q), _ptr(k_cache), _ptr(v_cache), ctypes.byref(desc), _ptr(block_tables), mbps,
+            _ptr(context_lens), S, int(max_context_len), float(scale), _ptr(out), pkv_dtype(out.dtype),
+            int(partition_size), _stream(dev)))
+    return out
+
+
 def paged_attn_decode_shared(q, k_cache, v_cache, block_tables, context_lens, scale, out, *,
                              max_context_len=None, partition_size=DEFAULT_PARTITION, workspace=None):
     """paged_attn_decode that reads blocks shared by neighbouring sequences once.
