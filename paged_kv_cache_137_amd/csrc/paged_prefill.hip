@@ -187,30 +187,30 @@ __global__ __launch_bounds__(256, 3) void prefill_kernel(const PrefillArgs a) {
   auto kswz = [](int row, int ch) { return D == 128 ? ch ^ (row & 15) : ch ^ ((row >> 1) & 7); };
   auto vswz = [](int row, int ch) { return D == 128 ? ch ^ (4 * (row & 3)) : ch ^ (4 * ((row >> 1) & 1)); };
 
-  // Work item wi enumerates (head, item of that head); with the XCD remap each
-  // XCD walks a contiguous range of wi, so all query tiles of a (prompt, head)
-  // share one XCD's L2, which holds the K/V they all reread.
-  //  - Up to PREFILL_DENSE_PROMPTS prompts: a head's items are the query tiles
-  //    that exist, prompt after prompt in order of context length (prefix +
-  //    new tokens), longest first, ties by index, and each prompt's tiles
-  //    longest first.  The long causal rows start first, the short ones fill
-  //    the end, and no workgroup is spent on a tile past a prompt's end.  Each
-  //    workgroup ranks the prompts itself (one per lane).
-  //  - More prompts: every prompt gets num_qtiles items, in index order.
+  // Work items.  Consecutive workgroups go to the 8 XCDs in turn, so the grid
+  // is 8 slices, one per XCD, of heads_per_xcd * items_per_head items each.
+  // Slice x holds heads x, x + 8, x + 16, ...  Within a slice the items run
+  // prompt after prompt, and for each prompt every head's query tiles, longest
+  // first.  The prompts' order:
+  //  - up to PREFILL_DENSE_PROMPTS prompts: by context length (prefix + new
+  //    tokens), longest first, ties by index; each workgroup ranks the prompts
+  //    itself, one per lane.  The longest causal rows of every head start
+  //    first and the short ones fill the end.
+  //  - more prompts: index order, found by a prefix scan over the prompts in
+  //    chunks of 64.
+  // Only query tiles that exist get an item (a few items past the last tile
+  // return at once).  The heads of one prompt run side by side on one XCD,
+  // whose L2 holds the K/V that their query tiles reread.
   const int wg = blockIdx.x;
-#if PKV_PRE_XCD
-  const int wi = (wg & 7) * a.per_xcd + (wg >> 3);
-#else
-  const int wi = wg;
-#endif
-  if (wi >= a.total_items) return;
-  const int h = wi / a.items_per_head;
-  const int item = wi - h * a.items_per_head;
+  const int xcd = wg & 7;
+  const int k = wg >> 3;  // position in the slice
+  const int HX = a.heads_per_xcd;
+  if (k >= HX * a.items_per_head) return;
   const int lane = threadIdx.x & 63;
-  int pr, qt, L;
+  const int np = a.num_prompts;
+  int pr = -1, nq_p = 0, start_p = 0, L = 0;
   long long off = 0;  // row offset of the prompt: the sum of the earlier prompts' lengths
-  if (a.num_prompts <= PREFILL_DENSE_PROMPTS) {
-    const int np = a.num_prompts;
+  if (np <= PREFILL_DENSE_PROMPTS) {
     const int lj = lane < np ? max(a.prompt_lens[lane], 0) : 0;
     int key = lj;
     if constexpr (PAGED) {
@@ -224,19 +224,47 @@ __global__ __launch_bounds__(256, 3) void prefill_kernel(const PrefillArgs a) {
       const int ni = __builtin_amdgcn_readlane(nq, i);
       start += (ki > key || (ki == key && i < lane)) ? ni : 0;
     }
-    const unsigned long long hit = __ballot(lane < np && item >= start && item < start + nq);
-    if (hit == 0ull) return;  // past the last tile of this head
+    const unsigned long long hit = __ballot(lane < np && k >= HX * start && k < HX * (start + nq));
+    if (hit == 0ull) return;  // past the last tile of the slice
     pr = (int)__builtin_ctzll(hit);
     L = __builtin_amdgcn_readlane(lj, pr);
-    qt = __builtin_amdgcn_readlane(nq, pr) - 1 - (item - __builtin_amdgcn_readlane(start, pr));
+    nq_p = __builtin_amdgcn_readlane(nq, pr);
+    start_p = __builtin_amdgcn_readlane(start, pr);
     off = lane < pr ? lj : 0;
   } else {
-    pr = item / a.num_qtiles;
-    qt = a.num_qtiles - 1 - (item - pr * a.num_qtiles);
-    L = a.prompt_lens[pr];
-    if (L <= qt * BM) return;
-    for (int i = lane; i < pr; i += 64) off += max(a.prompt_lens[i], 0);
+    int base = 0;  // tiles of the earlier chunks
+    for (int c0 = 0; c0 < np; c0 += 64) {
+      const int i = c0 + lane;
+      const int lj = i < np ? max(a.prompt_lens[i], 0) : 0;
+      const int nq = (int)(((int64_t)lj + BM - 1) / BM);
+      int incl = nq;  // inclusive prefix sum of the chunk's tile counts
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int y = __shfl_up(incl, d, 64);
+        if (lane >= d) incl += y;
+      }
+      const int tot = __builtin_amdgcn_readlane(incl, 63);
+      const int excl = base + incl - nq;
+      if (k < HX * (base + tot)) {
+        const unsigned long long hit = __ballot(i < np && k >= HX * excl && k < HX * (excl + nq));
+        const int pl = (int)__builtin_ctzll(hit);  // nonempty: k lies in this chunk
+        pr = c0 + pl;
+        L = __builtin_amdgcn_readlane(lj, pl);
+        nq_p = __builtin_amdgcn_readlane(nq, pl);
+        start_p = __builtin_amdgcn_readlane(excl, pl);
+        off += lane < pl ? lj : 0;
+        break;
+      }
+      base += tot;
+      off += lj;
+    }
+    if (pr < 0) return;  // past the last tile of the slice
   }
+  const int rem = k - HX * start_p;
+  const int hl = rem / nq_p;
+  const int h = xcd + 8 * hl;
+  if (h >= a.num_heads) return;
+  const int qt = nq_p - 1 - (rem - hl * nq_p);
   const int m0 = qt * BM;
   L = __builtin_amdgcn_readfirstlane(L);  // one value for the workgroup (keeps descriptors scalar)
 #pragma unroll
@@ -514,7 +542,7 @@ __global__ __launch_bounds__(256, 3) void prefill_kernel(const PrefillArgs a) {
 
 template <typename E, typename O, int D, int PB>
 static hipError_t prefill_t(const PrefillArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL((prefill_kernel<E, O, D, PB>), dim3(a.per_xcd * 8), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((prefill_kernel<E, O, D, PB>), dim3(a.total_items), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

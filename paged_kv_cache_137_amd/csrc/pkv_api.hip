@@ -459,7 +459,8 @@ int pkv_paged_attn_prefill(const void* q, const void* k, const void* v, int32_t 
     return PKV_EINVAL;
   const int32_t num_qtiles = (max_prompt_len + pkv::PREFILL_BLOCK_M - 1) / pkv::PREFILL_BLOCK_M;
   const int64_t per_head = pkv::prefill_items_per_head(num_prompts, num_qtiles, total_tokens);
-  const int64_t items = per_head * num_heads;
+  const int64_t heads_per_xcd = (num_heads + 7) / 8;
+  const int64_t items = 8 * heads_per_xcd * per_head;
   if (items > ((int64_t)1 << 31) - 64) return PKV_EINVAL;
   int st = device_status();
   if (st != PKV_OK) return st;
@@ -486,8 +487,8 @@ int pkv_paged_attn_prefill(const void* q, const void* k, const void* v, int32_t 
   a.max_prompt_len = max_prompt_len;
   a.num_qtiles = num_qtiles;
   a.items_per_head = (int32_t)per_head;
+  a.heads_per_xcd = (int32_t)heads_per_xcd;
   a.total_items = (int32_t)items;
-  a.per_xcd = (int32_t)((items + 7) / 8);
   a.scale_log2 = scale * 1.4426950408889634f;
   return launch_status(pkv::launch_prefill(a, dtype, out_dtype, head_dim, sm));
 }
@@ -514,7 +515,8 @@ int pkv_paged_attn_prefill_cached(const void* q, const void* k_cache, const void
     return PKV_EINVAL;
   const int32_t num_qtiles = (max_prompt_len + pkv::PREFILL_BLOCK_M - 1) / pkv::PREFILL_BLOCK_M;
   const int64_t per_head = pkv::prefill_items_per_head(num_prompts, num_qtiles, total_tokens);
-  const int64_t items = per_head * desc->num_heads;
+  const int64_t heads_per_xcd = (desc->num_heads + 7) / 8;
+  const int64_t items = 8 * heads_per_xcd * per_head;
   if (items > ((int64_t)1 << 31) - 64) return PKV_EINVAL;
   st = device_status();
   if (st != PKV_OK) return st;
@@ -553,8 +555,8 @@ int pkv_paged_attn_prefill_cached(const void* q, const void* k_cache, const void
   a.max_prompt_len = max_prompt_len;
   a.num_qtiles = num_qtiles;
   a.items_per_head = (int32_t)per_head;
+  a.heads_per_xcd = (int32_t)heads_per_xcd;
   a.total_items = (int32_t)items;
-  a.per_xcd = (int32_t)((items + 7) / 8);
   a.scale_log2 = scale * 1.4426950408889634f;
   return launch_status(pkv::launch_prefill(a, desc->dtype, out_dtype, desc->head_dim, sm));
 }

@@ -74,9 +74,9 @@ struct PrefillArgs {
   int32_t num_heads;
   int32_t max_prompt_len;
   int32_t num_qtiles;      // query tiles of the longest prompt
-  int32_t items_per_head;  // work items per head (see the prefill kernel)
-  int32_t total_items;     // items_per_head * num_heads
-  int32_t per_xcd;         // ceil(total_items / 8): work items per XCD slice of the grid
+  int32_t items_per_head;  // work items per head: a bound on the query tiles of one head
+  int32_t heads_per_xcd;   // ceil(num_heads / 8): heads of one XCD's slice of the grid
+  int32_t total_items;     // 8 * heads_per_xcd * items_per_head: the grid
   float scale_log2;
 };
 
@@ -112,16 +112,15 @@ hipError_t launch_prefill(const PrefillArgs& a, int dtype, int out_dtype, int he
 
 // Prefill query-tile height (rows per workgroup).
 constexpr int PREFILL_BLOCK_M = 128;
-// Up to this many prompts, the prefill enumerates only the query tiles that
-// exist, prompts ordered longest first (the kernel ranks them).
+// Up to this many prompts, each prefill workgroup ranks the prompts by length
+// (longest first); beyond it they run in index order.
 constexpr int PREFILL_DENSE_PROMPTS = 64;
 
-// Work items per head of the prefill grid: with few prompts, at most
-// ceil(total_tokens / BM) + num_prompts tiles exist (lengths summing to
-// total_tokens); otherwise every prompt gets num_qtiles items.
+// Work items per head of the prefill grid: the query tiles of one head, at
+// most ceil(total_tokens / BM) + num_prompts for lengths summing to
+// total_tokens, and at most num_prompts * num_qtiles.
 inline int64_t prefill_items_per_head(int32_t num_prompts, int32_t num_qtiles, int64_t total_tokens) {
   const int64_t sparse = (int64_t)num_prompts * num_qtiles;
-  if (num_prompts > PREFILL_DENSE_PROMPTS) return sparse;
   const int64_t dense = (total_tokens + PREFILL_BLOCK_M - 1) / PREFILL_BLOCK_M + num_prompts;
   return dense < sparse ? dense : sparse;
 }

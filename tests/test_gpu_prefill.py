@@ -64,6 +64,25 @@ def test_prefill_many_prompts_dense_and_sparse_enumeration(n):
     assert err <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("n,H", [(256, 12), (100, 8)])
+def test_prefill_many_ragged_prompts(n, H):
+    """More prompts than the workgroup ranks (prompts then run in index order,
+    found by a prefix scan in chunks of 64): ragged lengths with empty,
+    one-token and tile-multiple prompts, and a head count that leaves some XCD
+    slices with fewer heads, against the oracle on every output."""
+    rng = np.random.default_rng(90 + n)
+    lens = [int(x) for x in rng.integers(0, 700, size=n)]
+    lens[3], lens[10], lens[11], lens[77] = 0, 1, 128, 256
+    print(f"prefill {n} prompts x {H} heads, total {sum(lens)}", flush=True)
+    p = W.make_prefill(91, "bf16", H, 128, lens)
+    out32 = down(_prefill(p))
+    ref = oracle.attention.causal_prefill(p.q, p.k, p.v, p.prompt_lens, 1 / math.sqrt(128), "bf16")
+    assert np.isfinite(out32).all()
+    err = float(np.abs(out32 - ref).max())
+    print(f"  max|err|={err:.3e}", flush=True)
+    assert err <= TOL["bf16"]
+
+
 def test_prefill_last_row_matches_decode():
     print("prefill <-> decode consistency", flush=True)
     dt, H, D, L = "bf16", 4, 128, 777
