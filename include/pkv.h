@@ -121,14 +121,19 @@ int pkv_kv_cache_write(const void* k, const void* v, const int64_t* slot_mapping
                        void* k_cache, void* v_cache, const pkv_cache_desc* desc, void* stream);
 
 /*
- * Workspace for pkv_paged_attn_decode, in bytes.  P = ceil(max_context_len /
- * partition_size), or 1 when partition_size == 0.  PKV_PARTITION_AUTO is
- * resolved exactly as the decode resolves it for the same arguments.  The
- * workspace holds:
+ * Workspace for pkv_paged_attn_decode (and its other forms), in bytes.
+ * P = ceil(max_context_len / partition_size), or 1 when partition_size == 0.
+ * PKV_PARTITION_AUTO is resolved exactly as the decode resolves it for the
+ * same arguments.  With W = ceil(num_seqs / 4) windows, the workspace holds,
+ * each region 16-byte aligned:
  *   - a work counter (16 B);
- *   - the list of (sequence, partition) units (num_seqs * P int32);
- *   - when P > 1, the partial results of the split-context decode in float32
- *     (num_seqs * num_heads * P * (head_dim + 2) * 4 B).
+ *   - the list of units, (num_seqs + W) * P int32;
+ *   - partial results in float32: P + 1 slots per (sequence, head), each
+ *     head_dim values plus a running max and sum
+ *     (num_seqs * num_heads * (P + 1) * (head_dim + 2) * 4 B);
+ *   - the first token each sequence attends to on its own (num_seqs int32) and
+ *     one record per window (W int32), for the sharing the one-call decode
+ *     finds.
  * Its contents need no initialisation.  Each call rebuilds what it uses.
  * Returns 0 only for an empty or invalid shape.
  */
@@ -212,12 +217,26 @@ int pkv_decode_partition_for_lengths(const int32_t* context_lens, int32_t num_se
  *   workspace     device scratch of at least pkv_decode_workspace_bytes(...),
  *                 owned by the caller.  Calls that can run at the same time
  *                 (different streams) need separate workspaces.
+ * Blocks that neighbouring sequences share are read once for all of them
+ * ("vLLM & PagedAttention ...", section VII: parallel samples and common
+ * prefixes map their first logical blocks onto the same physical blocks).
+ * Sequences are taken in windows of four consecutive ones (0-3, 4-7, ...).
+ * In a window, the sequences whose first block id equals that of the window's
+ * first sequence holding a full block form a group, if there are two or more.
+ * The group's J leading full blocks that all members hold with the same ids
+ * (inside every member's context) are read once, with one online softmax per
+ * member's query; each member then attends to its remaining tokens on its
+ * own.  Nothing is assumed about the tables: the sharing is found on the
+ * device at every call, and a batch without it runs exactly as before.
  * Work is spread by a small plan kernel and a persistent kernel that claims
- * units from a counter in the workspace.  No arithmetic depends on that order,
- * and the merge order of partitions is fixed, so results are deterministic,
- * bit for bit.  The output does not depend on which physical ids hold the
- * blocks, or on whether blocks are shared.  A table entry outside [0, num_blocks) makes that
- * sequence's output NaN instead of reading out of bounds.
+ * units from a counter in the workspace; a reduce kernel then merges the
+ * partial results of split contexts and sharing groups in a fixed order.  No
+ * arithmetic depends on which workgroup ran a unit, so results are
+ * deterministic, bit for bit, and do not depend on which physical ids hold the
+ * blocks.  Whether blocks are shared changes only the order of the fp32 sums
+ * (a group's shared blocks form partial results of their own).  A table entry
+ * outside [0, num_blocks) makes that sequence's output NaN instead of reading
+ * out of bounds.
  */
 int pkv_paged_attn_decode(const void* q, const void* k_cache, const void* v_cache, const pkv_cache_desc* desc,
                           const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
@@ -225,12 +244,15 @@ int pkv_paged_attn_decode(const void* q, const void* k_cache, const void* v_cach
                           int32_t partition_size, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * The two stages of pkv_paged_attn_decode, exposed so a caller can time or
- * overlap them.  The arguments are identical.  _partial launches the
- * per-partition kernel.  It writes `out` for sequences that fit one partition,
- * and the workspace for the others.  _reduce then merges the workspace into
- * `out`.  _partial followed by _reduce on one stream is the whole of
- * pkv_paged_attn_decode, bit for bit.
+ * The decode in two stages, exposed so a caller can time or overlap them.
+ * The arguments are identical to pkv_paged_attn_decode's.  This form does not
+ * look for shared blocks: every sequence reads its blocks through its own
+ * table.  _partial launches the plan and per-partition kernels.  It writes
+ * `out` for sequences that fit one partition, and the workspace for the
+ * others.  _reduce then merges the workspace into `out` (it launches nothing
+ * when no context is split).  _partial followed by _reduce on one stream is
+ * pkv_paged_attn_decode, bit for bit, for any batch in which no window's
+ * sequences share leading blocks; with sharing the two agree within rounding.
  */
 int pkv_paged_attn_decode_partial(const void* q, const void* k_cache, const void* v_cache,
                                   const pkv_cache_desc* desc, const int32_t* block_tables,
@@ -270,26 +292,11 @@ int pkv_paged_attn_decode_noalloc(const void* q, const void* k_cache, const void
                                   int32_t out_dtype, int32_t partition_size, void* stream);
 
 /*
- * pkv_paged_attn_decode_shared - pkv_paged_attn_decode for batches whose
- * sequences share leading blocks: parallel samples of one request, or
- * requests with a common prefix, whose tables hold the same physical ids for
- * those blocks ("vLLM & PagedAttention ...", section VII: blocks shared with
- * reference counts; "PagedAttention and vLLM, annotated", section 4.4).
- *
- * Arguments, preconditions, errors and result are those of
- * pkv_paged_attn_decode (the same value, up to the order of the fp32 sums),
- * except that the workspace must hold pkv_decode_shared_workspace_bytes(...).
- * Sequences are taken in windows of four consecutive ones (0-3, 4-7, ...).
- * In a window, the sequences whose first block id equals that of the window's
- * first sequence holding a full block form a group, if there are two or more.
- * The group's J leading full blocks that all members hold with the same ids
- * (inside every member's context) are read once, with one online softmax per
- * member's query.  Each member then attends to its remaining tokens on its
- * own, and a merge combines the partial results in a fixed order.  Nothing is
- * assumed about the tables: sharing is found on the device each call, and a
- * batch without it gives the plain decode's partitions.  Results are
- * deterministic, bit for bit.  PKV_PARTITION_AUTO resolves as for
- * pkv_paged_attn_decode.
+ * pkv_paged_attn_decode_shared and pkv_decode_shared_workspace_bytes are
+ * pkv_paged_attn_decode and pkv_decode_workspace_bytes under the names of the
+ * shared-prefix decode ("vLLM & PagedAttention ...", section VII), which the
+ * one-call decode now performs itself: same arguments, same result, same
+ * workspace.
  */
 size_t pkv_decode_shared_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
                                          int32_t max_context_len, int32_t partition_size);

@@ -63,28 +63,30 @@ bool copy_to_host(std::vector<T>& dst, const T* src, size_t n, hipStream_t st) {
 
 // Decode workspace, in this order (each region 16-byte aligned):
 //   work_ctrl  2 int32 (+ padding to 16 bytes)
-//   work_list  S * P int32
-//   ws_acc     S * H * P * D float   (only when P > 1)
-//   ws_ml      S * H * P * 2 float   (only when P > 1)
-// The shared-prefix form always has the partial regions (a sequence with one
-// partition of its own still merges it with its group's), followed by
+//   work_list  (S + W) * P int32, W = ceil(S / SHARE_WINDOW) windows
+//   ws_acc     S * H * (P + 1) * D float
+//   ws_ml      S * H * (P + 1) * 2 float
 //   tok_start  S int32
-//   win_info   W int32, W = ceil(S / SHARE_WINDOW)
-//   acc_sh     S * H * P * D float
-//   ml_sh      S * H * P * 2 float
+//   win_info   W int32
+// The one-call decode uses all of it: a sequence in a sharing group has up to
+// P + 1 partial results (its group's partitions, then its own).  The two-stage
+// form uses the counter, the first S * P list entries and P of the P + 1
+// slots.
 struct DecodePlan {
   int32_t part_blocks = 0;
   int32_t num_parts = 0;
   int32_t num_windows = 0;
-  size_t list_off = 0, acc_off = 0, ml_off = 0;
-  size_t start_off = 0, win_off = 0, acc_sh_off = 0, ml_sh_off = 0;
+  size_t list_off = 0, acc_off = 0, ml_off = 0, start_off = 0, win_off = 0;
   size_t ws_bytes = 0;
+  int64_t max_entries = 0;
 };
 
 size_t align16(size_t x) { return (x + 15) & ~(size_t)15; }
 
+constexpr int32_t kHeadsPerUnit = 4;  // heads one decode unit covers (the kernel's NW)
+
 DecodePlan plan_decode(int32_t num_seqs, int32_t num_heads, int32_t head_dim, int32_t max_context_len,
-                       int32_t partition_size, int32_t block_size = kBlock, bool shared = false) {
+                       int32_t partition_size, int32_t block_size = kBlock) {
   DecodePlan p;
   if (partition_size == 0) {
     p.part_blocks = (max_context_len + block_size - 1) / block_size;
@@ -93,20 +95,15 @@ DecodePlan plan_decode(int32_t num_seqs, int32_t num_heads, int32_t head_dim, in
     p.part_blocks = partition_size / block_size;
     p.num_parts = (max_context_len + partition_size - 1) / partition_size;
   }
-  const size_t units = (size_t)num_seqs * num_heads * p.num_parts;
-  const bool partials = shared || p.num_parts > 1;
+  p.num_windows = (num_seqs + pkv::SHARE_WINDOW - 1) / pkv::SHARE_WINDOW;
+  p.max_entries = ((int64_t)num_seqs + p.num_windows) * p.num_parts;
+  const size_t slots = (size_t)num_seqs * num_heads * (p.num_parts + 1);
   p.list_off = 16;
-  p.acc_off = p.list_off + align16((size_t)num_seqs * p.num_parts * sizeof(int32_t));
-  p.ml_off = p.acc_off + (partials ? units * head_dim * sizeof(float) : 0);
-  p.ws_bytes = p.ml_off + (partials ? units * 2 * sizeof(float) : 0);
-  if (shared) {
-    p.num_windows = (num_seqs + pkv::SHARE_WINDOW - 1) / pkv::SHARE_WINDOW;
-    p.start_off = align16(p.ws_bytes);
-    p.win_off = p.start_off + align16((size_t)num_seqs * sizeof(int32_t));
-    p.acc_sh_off = p.win_off + align16((size_t)p.num_windows * sizeof(int32_t));
-    p.ml_sh_off = p.acc_sh_off + units * head_dim * sizeof(float);
-    p.ws_bytes = p.ml_sh_off + units * 2 * sizeof(float);
-  }
+  p.acc_off = p.list_off + align16((size_t)p.max_entries * sizeof(int32_t));
+  p.ml_off = p.acc_off + slots * head_dim * sizeof(float);
+  p.start_off = align16(p.ml_off + slots * 2 * sizeof(float));
+  p.win_off = p.start_off + align16((size_t)num_seqs * sizeof(int32_t));
+  p.ws_bytes = p.win_off + (size_t)p.num_windows * sizeof(int32_t);
   return p;
 }
 
@@ -143,8 +140,10 @@ int32_t resolve_partition(int32_t partition_size, int32_t num_seqs, int32_t num_
   return (int32_t)size;
 }
 
-int decode_impl(int stages, bool shared, const void* q, const void* k_cache, const void* v_cache,
-                const pkv_cache_desc* desc,
+// stages: kBoth is the one-call decode (sharing found on the device, then
+// plan, decode and reduce); kPartial and kReduce are the two stages of the
+// two-stage form (no sharing; the reduce runs only for split contexts).
+int decode_impl(int stages, const void* q, const void* k_cache, const void* v_cache, const pkv_cache_desc* desc,
                 const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
                 int32_t num_seqs, int32_t max_context_len, float scale, void* out, int32_t out_dtype,
                 int32_t partition_size, void* workspace, size_t workspace_bytes, void* stream) {
@@ -154,19 +153,20 @@ int decode_impl(int stages, bool shared, const void* q, const void* k_cache, con
   const int32_t bsz = desc->block_size;
   if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * bsz) return PKV_EINVAL;
   if (out_dtype != PKV_F32 && out_dtype != desc->dtype) return PKV_ENOTSUP;
-  partition_size = resolve_partition(partition_size, num_seqs, desc->num_heads, max_context_len, shared);
+  partition_size = resolve_partition(partition_size, num_seqs, desc->num_heads, max_context_len, false);
   if (partition_size != 0 && (partition_size % bsz != 0 || partition_size < 16 || partition_size > 4096))
     return PKV_EINVAL;
   if (num_seqs == 0) return PKV_OK;
   if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out) return PKV_EINVAL;
   if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16)) return PKV_EINVAL;
   if (!aligned(block_tables, 4) || !aligned(context_lens, 4)) return PKV_EINVAL;
-  const DecodePlan plan =
-      plan_decode(num_seqs, desc->num_heads, desc->head_dim, max_context_len, partition_size, bsz, shared);
-  const int64_t units = (int64_t)num_seqs * desc->num_heads * plan.num_parts;
-  if (units > ((int64_t)1 << 31) - 64 || num_seqs > 65535 * 32768) return PKV_EINVAL;
-  if ((int64_t)num_seqs * plan.num_parts >= ((int64_t)1 << 30)) return PKV_EINVAL;  // work-list entries carry a tag bit
-  if (desc->num_heads > 65535) return PKV_EINVAL;
+  if (desc->num_heads > 65535 || num_seqs > (1 << 24)) return PKV_EINVAL;
+  const DecodePlan plan = plan_decode(num_seqs, desc->num_heads, desc->head_dim, max_context_len, partition_size, bsz);
+  const int64_t groups = (desc->num_heads + kHeadsPerUnit - 1) / kHeadsPerUnit;
+  // Work-list entries carry two flag bits, and the kernel counts units
+  // (entries x head groups) in int32.
+  if (plan.max_entries >= ((int64_t)1 << 29) || plan.max_entries * groups > ((int64_t)1 << 31) - 64)
+    return PKV_EINVAL;
   if (workspace == nullptr || !aligned(workspace, 16)) return PKV_EINVAL;
   if (workspace_bytes < plan.ws_bytes) return PKV_EWORKSPACE;
   st = device_status();
@@ -187,6 +187,7 @@ int decode_impl(int stages, bool shared, const void* q, const void* k_cache, con
     }
   }
 
+  const bool one_call = stages == kBoth;
   pkv::DecodeArgs a{};
   a.q = q;
   a.k_cache = k_cache;
@@ -197,14 +198,11 @@ int decode_impl(int stages, bool shared, const void* q, const void* k_cache, con
   char* ws = reinterpret_cast<char*>(workspace);
   a.work_ctrl = reinterpret_cast<int32_t*>(ws);
   a.work_list = reinterpret_cast<int32_t*>(ws + plan.list_off);
-  const bool partials = shared || plan.num_parts > 1;
-  a.ws_acc = partials ? reinterpret_cast<float*>(ws + plan.acc_off) : nullptr;
-  a.ws_ml = partials ? reinterpret_cast<float*>(ws + plan.ml_off) : nullptr;
-  if (shared) {
+  a.ws_acc = reinterpret_cast<float*>(ws + plan.acc_off);
+  a.ws_ml = reinterpret_cast<float*>(ws + plan.ml_off);
+  if (one_call) {
     a.tok_start = reinterpret_cast<int32_t*>(ws + plan.start_off);
     a.win_info = reinterpret_cast<int32_t*>(ws + plan.win_off);
-    a.ws_acc_sh = reinterpret_cast<float*>(ws + plan.acc_sh_off);
-    a.ws_ml_sh = reinterpret_cast<float*>(ws + plan.ml_sh_off);
     a.num_windows = plan.num_windows;
   }
   a.num_blocks = desc->num_blocks;
@@ -215,19 +213,17 @@ int decode_impl(int stages, bool shared, const void* q, const void* k_cache, con
   a.block_size = bsz;
   a.part_blocks = plan.part_blocks;
   a.num_parts = plan.num_parts;
-  a.total_units = (int32_t)units;
+  a.num_slots = plan.num_parts + 1;
+  a.max_entries = (int32_t)(one_call ? plan.max_entries : (int64_t)num_seqs * plan.num_parts);
   a.scale_log2 = scale * 1.4426950408889634f;
 
-  if (shared) {
-    st = launch_status(pkv::launch_decode_shared_partial(a, desc->dtype, out_dtype, desc->head_dim, sm));
-    if (st != PKV_OK) return st;
-    return launch_status(pkv::launch_decode_shared_reduce(a, out_dtype, desc->head_dim, sm));
-  }
   if (stages & kPartial) {
     st = launch_status(pkv::launch_decode_partial(a, desc->dtype, out_dtype, desc->head_dim, sm));
     if (st != PKV_OK) return st;
   }
-  if ((stages & kReduce) && plan.num_parts > 1) {
+  // The one-call decode merges whenever a sequence may have more than one
+  // partial result: split contexts, or a sharing group (found on the device).
+  if ((stages & kReduce) && (one_call || plan.num_parts > 1)) {
     st = launch_status(pkv::launch_decode_reduce(a, out_dtype, desc->head_dim, sm));
     if (st != PKV_OK) return st;
   }
@@ -380,7 +376,7 @@ size_t pkv_decode_shared_workspace_bytes(int32_t num_seqs, int32_t num_heads, in
   if (num_seqs <= 0 || num_heads <= 0 || head_dim <= 0 || max_context_len <= 0) return 0;
   partition_size = resolve_partition(partition_size, num_seqs, num_heads, max_context_len, true);
   if (partition_size < 0) return 0;
-  return plan_decode(num_seqs, num_heads, head_dim, max_context_len, partition_size, kBlock, true).ws_bytes;
+  return plan_decode(num_seqs, num_heads, head_dim, max_context_len, partition_size).ws_bytes;
 }
 
 int pkv_paged_attn_decode_shared(const void* q, const void* k_cache, const void* v_cache, const pkv_cache_desc* desc,
@@ -388,7 +384,7 @@ int pkv_paged_attn_decode_shared(const void* q, const void* k_cache, const void*
                                  int32_t num_seqs, int32_t max_context_len, float scale, void* out,
                                  int32_t out_dtype, int32_t partition_size, void* workspace, size_t workspace_bytes,
                                  void* stream) {
-  return decode_impl(kBoth, true, q, k_cache, v_cache, desc, block_tables, max_blocks_per_seq, context_lens,
+  return decode_impl(kBoth, q, k_cache, v_cache, desc, block_tables, max_blocks_per_seq, context_lens,
                      num_seqs, max_context_len, scale, out, out_dtype, partition_size, workspace, workspace_bytes,
                      stream);
 }
@@ -397,7 +393,7 @@ int pkv_paged_attn_decode(const void* q, const void* k_cache, const void* v_cach
                           const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
                           int32_t num_seqs, int32_t max_context_len, float scale, void* out, int32_t out_dtype,
                           int32_t partition_size, void* workspace, size_t workspace_bytes, void* stream) {
-  return decode_impl(kBoth, false, q, k_cache, v_cache, desc, block_tables, max_blocks_per_seq, context_lens, num_seqs,
+  return decode_impl(kBoth, q, k_cache, v_cache, desc, block_tables, max_blocks_per_seq, context_lens, num_seqs,
                      max_context_len, scale, out, out_dtype, partition_size, workspace, workspace_bytes, stream);
 }
 
@@ -419,7 +415,7 @@ int pkv_paged_attn_decode_noalloc(const void* q, const void* k_cache, const void
   if (hipGetDevice(&dev) != hipSuccess) return PKV_EDEVICE;
   void* ws = scratch_ptr(dev);
   if (ws == nullptr) return PKV_EDEVICE;
-  return decode_impl(kBoth, false, q, k_cache, v_cache, desc, block_tables, max_blocks_per_seq, context_lens,
+  return decode_impl(kBoth, q, k_cache, v_cache, desc, block_tables, max_blocks_per_seq, context_lens,
                      num_seqs, max_context_len, scale, out, out_dtype, part, ws, PKV_NOALLOC_SCRATCH_BYTES, stream);
 }
 
@@ -428,7 +424,7 @@ int pkv_paged_attn_decode_partial(const void* q, const void* k_cache, const void
                                   int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
                                   int32_t max_context_len, float scale, void* out, int32_t out_dtype,
                                   int32_t partition_size, void* workspace, size_t workspace_bytes, void* stream) {
-  return decode_impl(kPartial, false, q, k_cache, v_cache, desc, block_tables, max_blocks_per_seq, context_lens, num_seqs,
+  return decode_impl(kPartial, q, k_cache, v_cache, desc, block_tables, max_blocks_per_seq, context_lens, num_seqs,
                      max_context_len, scale, out, out_dtype, partition_size, workspace, workspace_bytes, stream);
 }
 
@@ -437,7 +433,7 @@ int pkv_paged_attn_decode_reduce(const void* q, const void* k_cache, const void*
                                  int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
                                  int32_t max_context_len, float scale, void* out, int32_t out_dtype,
                                  int32_t partition_size, void* workspace, size_t workspace_bytes, void* stream) {
-  return decode_impl(kReduce, false, q, k_cache, v_cache, desc, block_tables, max_blocks_per_seq, context_lens, num_seqs,
+  return decode_impl(kReduce, q, k_cache, v_cache, desc, block_tables, max_blocks_per_seq, context_lens, num_seqs,
                      max_context_len, scale, out, out_dtype, partition_size, workspace, workspace_bytes, stream);
 }
 

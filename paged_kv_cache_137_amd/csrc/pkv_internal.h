@@ -21,7 +21,7 @@ struct WriteArgs {
   int32_t block_shift;  // log2(tokens per block)
 };
 
-// Arguments shared by the two decode stages.
+// Arguments of the decode kernels.
 struct DecodeArgs {
   const void* q;
   const void* k_cache;
@@ -29,18 +29,15 @@ struct DecodeArgs {
   const int32_t* block_tables;
   const int32_t* context_lens;
   void* out;
-  float* ws_acc;      // [S][H][P][D] unnormalised partial outputs
-  float* ws_ml;       // [S][H][P][2]  running max (log2 units) and sum
-  int32_t* work_list; // [S*P] (sequence, partition) entries, largest partitions first
-  int32_t* work_ctrl; // [0] next unit to claim, [1] number of entries in work_list,
-                      // [2] next shared-prefix unit to claim
-  // Shared-prefix form only (null otherwise): sequences are taken in windows
-  // of SHARE_WINDOW consecutive ones; the members of a window that hold the
-  // same leading blocks form a group whose shared blocks are read once.
+  float* ws_acc;      // [S][H][num_slots][D] unnormalised partial outputs
+  float* ws_ml;       // [S][H][num_slots][2]  running max (log2 units) and sum
+  int32_t* work_list; // units' entries, largest first: (index << 2) | flags
+  int32_t* work_ctrl; // [0] next unit to claim, [1] number of entries in work_list
+  // Sharing (null when the call does not look for it): sequences are taken in
+  // windows of SHARE_WINDOW consecutive ones; the members of a window that
+  // hold the same leading blocks form a group whose shared blocks are read once.
   int32_t* tok_start; // [S] first token a sequence attends to on its own (0: no group)
   int32_t* win_info;  // [W] (shared full blocks J << 4) | member mask, or 0
-  float* ws_acc_sh;   // [S][H][P][D] partial outputs over the shared blocks
-  float* ws_ml_sh;    // [S][H][P][2]
   int32_t num_windows;
   int64_t num_blocks;
   int32_t num_heads;
@@ -50,7 +47,8 @@ struct DecodeArgs {
   int32_t block_size;   // tokens per block: 8, 16 or 32
   int32_t part_blocks;  // blocks per partition
   int32_t num_parts;    // P: partitions of the longest allowed context
-  int32_t total_units;  // upper bound on units: H * S * P
+  int32_t num_slots;    // partial results per (sequence, head): P + 1 (group partitions + own)
+  int32_t max_entries;  // bound on the work list: (S + W) * P
   float scale_log2;     // scale * log2(e)
 };
 
@@ -98,15 +96,13 @@ struct CopyArgs {
 // Each returns a hipError_t from the launch.
 hipError_t launch_copy_blocks(const CopyArgs& a, hipStream_t stream);
 hipError_t launch_kv_cache_write(const WriteArgs& a, hipStream_t stream);
+// The decode: detect (when sharing is looked for), plan and persistent decode
+// kernels; then the reduce, which merges partial results.
 hipError_t launch_decode_partial(const DecodeArgs& a, int dtype, int out_dtype, int head_dim, hipStream_t stream);
 hipError_t launch_decode_reduce(const DecodeArgs& a, int out_dtype, int head_dim, hipStream_t stream);
-// Shared-prefix decode: detection, plan, group and per-sequence kernels; then the merge.
-hipError_t launch_decode_shared_partial(const DecodeArgs& a, int dtype, int out_dtype, int head_dim,
-                                        hipStream_t stream);
-hipError_t launch_decode_shared_reduce(const DecodeArgs& a, int out_dtype, int head_dim, hipStream_t stream);
 
-// Sequences per sharing window of the shared-prefix decode (a group has at
-// most this many members).
+// Sequences per sharing window of the decode (a group has at most this many
+// members).
 constexpr int SHARE_WINDOW = 4;
 hipError_t launch_prefill(const PrefillArgs& a, int dtype, int out_dtype, int head_dim, hipStream_t stream);
 

@@ -188,6 +188,11 @@ def paged_attn_decode(q, k_cache, v_cache, block_tables, context_lens, scale, ou
     (the table capacity), tables padded past 4096 tokens make a large batch
     split even when every real context is short; pass the real maximum when it
     is known.  Without a workspace, one is allocated through torch.
+
+    Leading blocks that neighbouring sequences share (parallel samples, a
+    common prefix: the same physical ids at the start of their tables, within
+    windows of four consecutive sequences) are found on the device and read
+    once for all of them.
     """
     return _decode_call("pkv_paged_attn_decode", q, k_cache, v_cache, block_tables, context_lens, scale, out,
                         max_context_len, partition_size, workspace)
@@ -230,27 +235,25 @@ def paged_attn_decode_noalloc(q, k_cache, v_cache, block_tables, context_lens, s
 
 def paged_attn_decode_shared(q, k_cache, v_cache, block_tables, context_lens, scale, out, *,
                              max_context_len=None, partition_size=DEFAULT_PARTITION, workspace=None):
-    """paged_attn_decode that reads blocks shared by neighbouring sequences once.
-
-    Same arguments and result as paged_attn_decode.  Within each window of four
-    consecutive sequences, those whose tables start with the same block ids
-    (parallel samples, a common prefix) have those blocks read once for all of
-    them.  The workspace is sized by decode_shared_workspace_bytes.
-    """
+    """paged_attn_decode under the shared-prefix decode's name: the one-call
+    decode reads shared leading blocks once itself.  Same arguments and result."""
     return _decode_call("pkv_paged_attn_decode_shared", q, k_cache, v_cache, block_tables, context_lens, scale,
                         out, max_context_len, partition_size, workspace)
 
 
 def paged_attn_decode_partial(q, k_cache, v_cache, block_tables, context_lens, scale, out, *,
                               max_context_len=None, partition_size=DEFAULT_PARTITION, workspace=None):
-    """First stage of paged_attn_decode (per-partition kernel only)."""
+    """First stage of the two-stage decode (plan and per-partition kernels).  The
+    two-stage form does not look for shared blocks; with the second stage it
+    equals paged_attn_decode bit for bit on batches without sharing."""
     return _decode_call("pkv_paged_attn_decode_partial", q, k_cache, v_cache, block_tables, context_lens, scale,
                         out, max_context_len, partition_size, workspace)
 
 
 def paged_attn_decode_reduce(q, k_cache, v_cache, block_tables, context_lens, scale, out, *,
                              max_context_len=None, partition_size=DEFAULT_PARTITION, workspace=None):
-    """Second stage of paged_attn_decode (split-context reduce only)."""
+    """Second stage of the two-stage decode (the split-context reduce; nothing
+    runs when no context is split)."""
     return _decode_call("pkv_paged_attn_decode_reduce", q, k_cache, v_cache, block_tables, context_lens, scale,
                         out, max_context_len, partition_size, workspace)
 

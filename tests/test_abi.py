@@ -55,32 +55,28 @@ def test_version_and_status_strings(lib):
     assert lib.pkv_status_str(12345) == b"unknown status"
 
 
-def test_workspace_sizing(lib):
-    # counter (16 B) + unit list (256 seqs x 8 partitions int32) + partials
-    # (256 seqs x 32 heads x ceil(4096/512)=8 partitions x (128 + 2) floats)
-    assert lib.pkv_decode_workspace_bytes(256, 32, 128, 4096, 512) == 16 + 256 * 8 * 4 + 256 * 32 * 8 * 130 * 4
-    assert lib.pkv_decode_workspace_bytes(256, 32, 128, 512, 512) == 16 + 256 * 4  # one partition: no partials
-    assert lib.pkv_decode_workspace_bytes(256, 32, 128, 4096, 0) == 16 + 256 * 4   # split disabled
-    assert lib.pkv_decode_workspace_bytes(3, 32, 128, 4096, 512) == 16 + 96 + 3 * 32 * 8 * 130 * 4
-    assert lib.pkv_decode_workspace_bytes(0, 32, 128, 4096, 512) == 0
-
-
-def test_shared_decode_workspace_sizing(lib):
-    # the plain layout with partial results always present, then per-sequence
-    # start tokens (S int32), window records (ceil(S/4) int32), and the group
-    # partials (S x H x P x (D + 2) floats); each region 16-byte aligned
+def _ws_layout(S, H, D, P):
+    """The decode workspace as include/pkv.h lays it out, region by region (16-byte aligned)."""
     a16 = lambda x: (x + 15) & ~15  # noqa: E731
-    S, H, D, P = 256, 32, 128, 8
-    plain = 16 + a16(S * P * 4) + S * H * P * (D + 2) * 4
-    want = a16(plain) + a16(S * 4) + a16((S + 3) // 4 * 4) + S * H * P * (D + 2) * 4
-    assert lib.pkv_decode_shared_workspace_bytes(S, H, D, 4096, 512) == want
-    # one partition: the partials are still there (a group member merges its own
-    # partition with its group's)
-    one = 16 + a16(S * 4) + S * H * (D + 2) * 4
-    assert lib.pkv_decode_shared_workspace_bytes(S, H, D, 512, 512) == (
-        a16(one) + a16(S * 4) + a16(S // 4 * 4) + S * H * (D + 2) * 4)
-    assert lib.pkv_decode_shared_workspace_bytes(0, H, D, 4096, 512) == 0
-    assert lib.pkv_decode_shared_workspace_bytes(S, H, D, 4096, 512) > lib.pkv_decode_workspace_bytes(S, H, D, 4096, 512)
+    W = (S + 3) // 4                 # windows of four sequences
+    slots = S * H * (P + 1)          # partial results: the group's partitions, then the sequence's own
+    off = 16 + a16((S + W) * P * 4)  # counter, then the work list of (S + W) * P entries
+    off += slots * D * 4             # unnormalised partial outputs
+    off = a16(off + slots * 2 * 4)   # (max, sum) per partial result
+    start = off
+    off += a16(S * 4)                # first own token per sequence
+    return start, off + W * 4        # window records
+
+
+def test_workspace_sizing(lib):
+    for S, H, D, mc, part, P in [(256, 32, 128, 4096, 512, 8), (256, 32, 128, 512, 512, 1),
+                                 (256, 32, 128, 4096, 0, 1), (3, 32, 128, 4096, 512, 8), (5, 40, 64, 2000, 256, 8)]:
+        want = _ws_layout(S, H, D, P)[1]
+        assert lib.pkv_decode_workspace_bytes(S, H, D, mc, part) == want, (S, H, D, mc, part)
+        # the shared-prefix call is the same call, with the same workspace
+        assert lib.pkv_decode_shared_workspace_bytes(S, H, D, mc, part) == want
+    assert lib.pkv_decode_workspace_bytes(0, 32, 128, 4096, 512) == 0
+    assert lib.pkv_decode_shared_workspace_bytes(0, 32, 128, 4096, 512) == 0
 
 
 def _part(lib, S, H, mc, p, shared=0):

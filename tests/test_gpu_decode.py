@@ -114,6 +114,40 @@ def test_decode_config3_bench_launch():
            outputs_compared=int(auto.numel()), bit_exact_equals_partition_0=True, oracle_seconds=round(t_or, 2))
 
 
+@pytest.mark.parametrize("cfg", [2, 4])
+def test_decode_merge_reads_fresh_partial_results(cfg):
+    """The one-call decode merges a sequence's partial results inside the decode
+    kernel, in the workgroup that delivers the last one; the others may run on
+    other XCDs.  The workspace is filled with NaN bytes before every call, so a
+    merge that read a partial result before its writer's stores were visible
+    would give NaN.  Config 2 splits contexts (up to 8 partitions at 256
+    tokens); config 4's parallel samples merge their group's partial results
+    with their own.  Every output against the oracle; repeated calls give the
+    same bits."""
+    print(f"decode merge freshness, config {cfg}", flush=True)
+    d = W.decode_config(cfg)
+    t = upload_decode(d)
+    ref, _ = refs.decode_ref(cfg, d)
+    for part in (256, 512, ops.PARTITION_AUTO):
+        ws = torch.empty(ops.decode_workspace_bytes(d.num_seqs, d.num_heads, d.head_dim, d.max_context_len, part),
+                         dtype=torch.uint8, device="cuda")
+        first = None
+        for rep in range(3):
+            ws.fill_(0xFF)
+            out = nan_out(d.q.shape)
+            ops.paged_attn_decode(t["q"], t["k_cache"], t["v_cache"], t["block_tables"], t["context_lens"], d.scale,
+                                  out, max_context_len=d.max_context_len, partition_size=part, workspace=ws)
+            got = down(out)
+            assert np.isfinite(got).all(), (part, rep)
+            err = float(np.abs(got - ref).max())
+            assert err <= TOL[d.dtype], (part, rep, err)
+            if first is None:
+                first = out
+            else:
+                assert torch.equal(out, first)
+        print(f"  partition {part}: max|err|={err:.3e}", flush=True)
+
+
 @pytest.mark.parametrize("dt", ["bf16", "f16"])
 def test_decode_auto_partition_splits_small_batches(dt):
     """Few sequences with long contexts: the automatic partition splits them, and
@@ -238,10 +272,14 @@ def test_decode_permutation_of_physical_ids_is_bit_exact():
 
 
 def test_decode_shared_blocks_equal_private_copies():
+    """Parallel samples that share their prompt's blocks, against the same batch
+    with private copies of every block.  The two-stage form (which reads every
+    sequence's blocks through its own table) gives the same bits; the one-call
+    decode reads the shared blocks once per group, a different order of the
+    fp32 sums, and agrees within the tolerance (both match the oracle)."""
     print("decode sharing vs private copies", flush=True)
     d = W.sharing_config(groups=16, samples=4)
     t = upload_decode(d)
-    shared = run_decode(ops, t, d, "f32")
     # private copies of every block, in a bigger pool
     S = d.num_seqs
     nbs = [-(-int(n) // 16) for n in d.context_lens]
@@ -256,8 +294,24 @@ def test_decode_shared_blocks_equal_private_copies():
             tables[s, j] = nxt; nxt += 1
     d2 = W.DecodeInputs(**{**d.__dict__, "k_cache": kc, "v_cache": vc, "block_tables": tables,
                            "num_blocks": kc.shape[0]})
-    private = run_decode(ops, upload_decode(d2), d2, "f32")
-    assert torch.equal(shared, private)
+    t2 = upload_decode(d2)
+
+    def two_stage(tt, dd):
+        out = nan_out(dd.q.shape)
+        ws = torch.empty(ops.decode_workspace_bytes(S, dd.num_heads, dd.head_dim, dd.max_context_len, 512),
+                         dtype=torch.uint8, device="cuda")
+        kw = dict(max_context_len=dd.max_context_len, partition_size=512, workspace=ws)
+        args = (tt["q"], tt["k_cache"], tt["v_cache"], tt["block_tables"], tt["context_lens"], dd.scale, out)
+        ops.paged_attn_decode_partial(*args, **kw)
+        ops.paged_attn_decode_reduce(*args, **kw)
+        return out
+
+    assert torch.equal(two_stage(t, d), two_stage(t2, d2))
+    shared = run_decode(ops, t, d, "f32")
+    private = run_decode(ops, t2, d2, "f32")
+    assert float((shared - private).abs().max()) <= TOL[d.dtype]
+    assert torch.equal(private, two_stage(t2, d2))  # without sharing, one call = two stages, bit for bit
+    _check(d, shared, None)
     assert d.info["physical_blocks_used"] < d.info["logical_blocks"]
 
 

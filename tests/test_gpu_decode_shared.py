@@ -108,12 +108,14 @@ def _run_shared(t, d, out_dtype="f32", partition_size=512, workspace=None, fill=
 
 
 def _starts_from_workspace(ws: torch.Tensor, S: int, H: int, D: int, max_ctx: int, part: int) -> np.ndarray:
-    """White-box read of the per-sequence start tokens in the shared workspace: the
-    plain decode's regions (counter, unit list, partial results), then tok_start."""
+    """White-box read of the per-sequence first own tokens in the decode
+    workspace (layout in include/pkv.h): counter, work list of (S + W) * P
+    entries, P + 1 partial results per (sequence, head), then tok_start."""
     P = 1 if part == 0 else -(-max_ctx // part)
+    W = (S + 3) // 4
     a16 = lambda x: (x + 15) & ~15  # noqa: E731
-    off = 16 + a16(S * P * 4) + S * H * P * D * 4 + S * H * P * 2 * 4
-    off = a16(off)
+    slots = S * H * (P + 1)
+    off = a16(16 + a16((S + W) * P * 4) + slots * D * 4 + slots * 2 * 4)
     return ws[off: off + 4 * S].cpu().numpy().view(np.int32).copy()
 
 
