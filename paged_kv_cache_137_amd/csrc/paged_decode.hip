@@ -15,17 +15,18 @@
 //    physical ids at the start of their tables, "vLLM & PagedAttention ...",
 //    section VII).  A group unit reads those blocks once and keeps one online
 //    softmax per member's query.
-//  - A detect kernel finds the groups (one wave per window of four
-//    sequences); a plan kernel (one workgroup) lists the units that hold
-//    tokens and sorts them by size, largest first, with a counting sort.  The
+//  - A plan kernel (one workgroup) finds the groups, lists the units that
+//    hold tokens and sorts them by size, largest first, with a counting sort.  The
 //    decode kernel is persistent: one NW-wave workgroup per CU (one wave per
 //    SIMD, which streams faster than full occupancy does) claims units from a
 //    counter until none are left.  Empty partitions cost nothing, and the ragged
 //    tail is spread over the whole GPU.
-//  - A sequence whose context is one unit writes its output directly.  The
-//    others write one partial result (running max, sum, unnormalised output)
-//    per unit, and a reduce kernel merges them in a fixed order, so no output
-//    depends on which workgroup ran which unit.
+//  - A sequence whose context is one unit writes its output directly; so do
+//    a group's members when contexts are not split (the group unit then also
+//    streams each member's own blocks).  The others write one partial result
+//    (running max, sum, unnormalised output) per unit, and a reduce kernel
+//    merges them in a fixed order, so no output depends on which workgroup ran
+//    which unit.
 //  - Inside a unit, wave w takes head NW*g + w alone and streams all of the
 //    partition's blocks for it.  A claim, the metadata lookups and the start of
 //    the load pipeline are thus shared by NW heads.
@@ -102,71 +103,115 @@ __device__ __forceinline__ int shared_parts(const DecodeArgs& a, int s, int part
   return (seq_start(a, s) + part_tokens - 1) / part_tokens;
 }
 
-// Sharing in window `win` (sequences SHARE_WINDOW*win ...), found by one wave.
-// The leader is the window's first sequence holding a full block; the members
-// are the window's sequences whose first block id is the leader's; J is the
-// number of leading full blocks that every member holds with the leader's ids,
-// all inside every member's context.  With two or more members and J >= 1 the
-// window is a group: win_info = (J << 4) | member mask, and each member's own
-// tokens start at J * block_size.  Otherwise win_info = 0 and they start at 0.
-__device__ void detect_window(const DecodeArgs& a, int win) {
+// Sharing, found by the plan workgroup.  Sequences are taken in windows of
+// SHARE_WINDOW consecutive ones.  The leader of a window is its first sequence
+// holding a full block; the members are the window's sequences whose first
+// block id is the leader's; J is the number of leading full blocks that every
+// member holds with the leader's ids, all inside every member's context.  With
+// two or more members and J >= 1 the window is a group: win_info =
+// (J << 4) | member mask, and each member's own tokens start at J * block_size.
+// Otherwise win_info = 0 and they start at 0.
+// Windows are handled in passes of DET_CAP.  In a pass, one thread per window
+// finds the leader, the members and the fewest full blocks among them (lim);
+// windows with fewer than two members are settled.  The others' J is the first
+// block, below lim, where some member's id differs from the leader's: threads
+// take (window, block) pairs, 64 blocks per round, and keep the minimum in LDS.
+constexpr int DET_CAP = 1024;
+struct DetectLds {
+  int win[DET_CAP], lead[DET_CAP], mask[DET_CAP], lim[DET_CAP], J[DET_CAP];
+  int ncand, maxlim;
+};
+
+__device__ void detect_all(const DecodeArgs& a, DetectLds& d) {
   constexpr int GW = SHARE_WINDOW;
-  const int lane = threadIdx.x & 63;
   const int BS = a.block_size;
-  const int s0 = win * GW;
-  int nfull[GW];
-  const int32_t* rows[GW];
+  const int tid = threadIdx.x;
+  const int nthr = blockDim.x;
+  for (int w0 = 0; w0 < a.num_windows; w0 += DET_CAP) {
+    if (tid == 0) {
+      d.ncand = 0;
+      d.maxlim = 0;
+    }
+    __syncthreads();
+    for (int k = tid; k < DET_CAP && w0 + k < a.num_windows; k += nthr) {
+      const int win = w0 + k;
+      const int s0 = win * GW;
+      int nfull[GW], first[GW];
 #pragma unroll
-  for (int i = 0; i < GW; ++i) {
-    const int s = s0 + i;
-    nfull[i] = s < a.num_seqs ? max(clamp_ctx(a, s), 0) / BS : 0;
-    rows[i] = a.block_tables + (int64_t)min(s, a.num_seqs - 1) * a.max_blocks_per_seq;
-  }
-  int lead = -1;
-#pragma unroll
-  for (int i = GW - 1; i >= 0; --i)
-    if (nfull[i] >= 1) lead = i;
-  int mask = 0, J = 0;
-  if (lead >= 0) {
-    const int32_t* lrow = a.block_tables + (int64_t)(s0 + lead) * a.max_blocks_per_seq;
-    const int first = lrow[0];
-    int lim = nfull[lead];
-    mask = 1 << lead;
-#pragma unroll
-    for (int i = 0; i < GW; ++i)
-      if (i != lead && nfull[i] >= 1 && rows[i][0] == first) {
-        mask |= 1 << i;
-        lim = min(lim, nfull[i]);
+      for (int i = 0; i < GW; ++i) {
+        const int s = s0 + i;
+        nfull[i] = s < a.num_seqs ? max(clamp_ctx(a, s), 0) / BS : 0;
+        first[i] = s < a.num_seqs ? a.block_tables[(int64_t)s * a.max_blocks_per_seq] : 0;
       }
-    if (__builtin_popcount(mask) >= 2) {
-      // The first block where some member's id differs from the leader's.
-      J = lim;
-      for (int j0 = 0; j0 < lim; j0 += 64) {
-        const int j = j0 + lane;
-        bool diff = false;
-        if (j < lim) {
-          const int lv = lrow[j];
+      int lead = -1;
 #pragma unroll
-          for (int i = 0; i < GW; ++i)
-            if ((mask >> i) & 1) diff |= rows[i][j] != lv;
-        }
-        const unsigned long long b = __ballot(diff);
-        if (b != 0ull) {
-          J = j0 + __builtin_ctzll(b);
-          break;
-        }
+      for (int i = GW - 1; i >= 0; --i)
+        if (nfull[i] >= 1) lead = i;
+      int mask = 0, lim = 0;
+      if (lead >= 0) {
+        int fl = first[0], nl = nfull[0];
+#pragma unroll
+        for (int i = 1; i < GW; ++i)
+          if (i == lead) {
+            fl = first[i];
+            nl = nfull[i];
+          }
+        lim = nl;
+#pragma unroll
+        for (int i = 0; i < GW; ++i)
+          if (nfull[i] >= 1 && first[i] == fl) {
+            mask |= 1 << i;
+            lim = min(lim, nfull[i]);
+          }
+      }
+      if (__builtin_popcount(mask) >= 2) {
+        const int c = atomicAdd(&d.ncand, 1);
+        d.win[c] = win;
+        d.lead[c] = s0 + lead;
+        d.mask[c] = mask;
+        d.lim[c] = lim;
+        d.J[c] = lim;
+        atomicMax(&d.maxlim, lim);
+      } else {
+        a.win_info[win] = 0;
+#pragma unroll
+        for (int i = 0; i < GW; ++i)
+          if (s0 + i < a.num_seqs) a.tok_start[s0 + i] = 0;
       }
     }
+    __syncthreads();
+    const int nc = d.ncand;
+    const int maxlim = d.maxlim;
+    for (int jr = 0; jr < maxlim; jr += 64) {
+      for (int q = tid; q < nc * 64; q += nthr) {
+        const int c = q >> 6;
+        const int j = jr + (q & 63);
+        if (j < d.lim[c] && j < d.J[c]) {  // d.J only shrinks; a stale read costs a redundant check
+          const int32_t* lrow = a.block_tables + (int64_t)d.lead[c] * a.max_blocks_per_seq;
+          const int32_t* wrow = a.block_tables + (int64_t)d.win[c] * GW * a.max_blocks_per_seq;
+          const int lv = lrow[j];
+          const int mask = d.mask[c];
+          bool diff = false;
+#pragma unroll
+          for (int i = 0; i < GW; ++i)
+            if ((mask >> i) & 1) diff |= wrow[(int64_t)i * a.max_blocks_per_seq + j] != lv;
+          if (diff) atomicMin(&d.J[c], j);
+        }
+      }
+      __syncthreads();
+    }
+    for (int c = tid; c < nc; c += nthr) {
+      const int win = d.win[c], mask = d.mask[c], J = d.J[c];
+      const bool grp = J >= 1;
+      a.win_info[win] = grp ? (J << 4) | mask : 0;
+#pragma unroll
+      for (int i = 0; i < GW; ++i) {
+        const int s = win * GW + i;
+        if (s < a.num_seqs) a.tok_start[s] = grp && ((mask >> i) & 1) ? J * BS : 0;
+      }
+    }
+    __syncthreads();
   }
-  const bool grp = __builtin_popcount(mask) >= 2 && J >= 1;
-  if (lane == 0) a.win_info[win] = grp ? (J << 4) | mask : 0;
-  if (lane < GW && s0 + lane < a.num_seqs) a.tok_start[s0 + lane] = grp && ((mask >> lane) & 1) ? J * BS : 0;
-}
-
-// Sharing detection of the one-call decode: one wave per window.
-__global__ __launch_bounds__(1024) void share_detect_kernel(const DecodeArgs a) {
-  const int win = blockIdx.x * 16 + (threadIdx.x >> 6);
-  if (win < a.num_windows) detect_window(a, win);
 }
 
 // The plan: list every unit that holds tokens (a sequence's own partitions
@@ -175,10 +220,12 @@ __global__ __launch_bounds__(1024) void share_detect_kernel(const DecodeArgs a) 
 // (partition 0, in the smallest bucket) so that its output is written as NaN.
 __global__ __launch_bounds__(1024) void decode_plan_kernel(const DecodeArgs a) {
   __shared__ int cnt[PLAN_BUCKETS];
+  __shared__ DetectLds det;
   const int BS = a.block_size;
   const int part_tokens = a.part_blocks * BS;
   const int P = a.num_parts;
   for (int i = threadIdx.x; i < PLAN_BUCKETS; i += blockDim.x) cnt[i] = 0;
+  if (a.win_info != nullptr) detect_all(a, det);  // ends with a barrier
   __syncthreads();
   // Pair i < npairs is (sequence i / P, partition i % P); pair npairs + j is
   // (window j / P, partition j % P) of the shared blocks.  Each gets a bucket
@@ -200,10 +247,17 @@ __global__ __launch_bounds__(1024) void decode_plan_kernel(const DecodeArgs a) {
       const int p = j - win * P;
       const int info = a.win_info[win];
       if (info == 0) return;
+      const int J = info >> 4;
       const int tok0 = p * part_tokens;
-      const int tend = min(tok0 + part_tokens, (info >> 4) * BS);
+      const int tend = min(tok0 + part_tokens, J * BS);
       if (tok0 >= tend) return;
-      bucket = min((tend - tok0) / BS, PLAN_BUCKETS - 1);
+      int nb = (tend - tok0) / BS;
+      if (P == 1) {  // unsplit: the group unit also streams each member's own blocks
+#pragma unroll
+        for (int g = 0; g < SHARE_WINDOW; ++g)
+          if ((info >> g) & 1) nb += (clamp_ctx(a, win * SHARE_WINDOW + g) + BS - 1) / BS - J;
+      }
+      bucket = min(nb, PLAN_BUCKETS - 1);
       entry = (j << ENTRY_SHIFT) | ENTRY_GROUP;
       return;
     }
@@ -222,6 +276,7 @@ __global__ __launch_bounds__(1024) void decode_plan_kernel(const DecodeArgs a) {
       return;
     }
     if (t0 >= ctx) return;
+    if (P == 1 && t0 > 0) return;  // a group member's own blocks: its group unit streams them
     const int nb = (min(part_tokens, ctx - t0) + BS - 1) / BS;
     const int lb = t0 / BS;
     const int32_t* row = a.block_tables + (int64_t)s * a.max_blocks_per_seq + lb;
@@ -289,14 +344,136 @@ __global__ __launch_bounds__(1024) void decode_plan_kernel(const DecodeArgs a) {
   }
 }
 
+// Stream the (block, head) tiles of table entries trow[0 .. nblk-1] through
+// consume(k tile, v tile, entry index, bad id): lane l's 16-byte pieces of
+// tile rows, two tiles in flight per wave (ping-pong register sets) while a
+// tile takes at most four loads.  An id outside the pool is never read; its
+// tile is consumed with `bad` set.
+template <typename G, bool NT, typename F>
+__device__ __forceinline__ void stream_tiles(const DecodeArgs& a, const int32_t* trow, int nblk, const char* kbase,
+                                             const char* vbase, int64_t bstride, F&& consume) {
+  constexpr int NI = G::NI;
+  const int lane = threadIdx.x & 63;
+  auto load = [&](int phys, uint4 (&kx)[NI], uint4 (&vx)[NI]) {
+    const char* kp = kbase + (int64_t)phys * bstride;
+    const char* vp = vbase + (int64_t)phys * bstride;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) kx[i] = load_kv16<NT>(kp + i * 1024);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) vx[i] = load_kv16<NT>(vp + i * 1024);
+  };
+  for (int cb = 0; cb < nblk; cb += 64) {
+    const int cn = min(64, nblk - cb);
+    // The chunk's table entries, one per lane; a wave-uniform readlane picks each.
+    const int tv = lane < cn ? trow[cb + lane] : 0;
+    auto phys_of = [&](int j, bool& bad) {
+      const int ph = __builtin_amdgcn_readlane(tv, j);
+      bad = (uint64_t)(uint32_t)ph >= (uint64_t)a.num_blocks;
+      return bad ? 0 : ph;
+    };
+    int j = 0;
+    if constexpr (G::PINGPONG) {
+      uint4 kA[NI], vA[NI], kB[NI], vB[NI];
+      bool badA, badB;
+      load(phys_of(j, badA), kA, vA);
+      while (j + 2 < cn) {
+        load(phys_of(j + 1, badB), kB, vB);
+        consume(kA, vA, cb + j, badA);
+        load(phys_of(j + 2, badA), kA, vA);
+        consume(kB, vB, cb + j + 1, badB);
+        j += 2;
+      }
+      if (j + 1 < cn) {
+        load(phys_of(j + 1, badB), kB, vB);
+        consume(kA, vA, cb + j, badA);
+        consume(kB, vB, cb + j + 1, badB);
+      } else {
+        consume(kA, vA, cb + j, badA);
+      }
+    } else {
+      for (; j < cn; ++j) {
+        uint4 kA[NI], vA[NI];
+        bool badA;
+        load(phys_of(j, badA), kA, vA);
+        consume(kA, vA, cb + j, badA);
+      }
+    }
+  }
+}
+
+// One lane row's online-softmax step over a tile of BS token rows: scores
+// q.k (log2 units), masked by selection at or past ctx (tb = the tile's first
+// position), NaN for a bad id; then the running max, sum and accumulators.
+template <typename E, int D, int BS>
+__device__ __forceinline__ void softmax_tile(const DecodeArgs& a, const uint4& qv, const uint4 (&kx)[DecodeGeom<E, D, BS>::NI],
+                                             uint4 (&vx)[DecodeGeom<E, D, BS>::NI], int tb, int ctx, bool bad,
+                                             float& m, float& l, float (&acc)[DecodeGeom<E, D, BS>::VEC]) {
+  using G = DecodeGeom<E, D, BS>;
+  using C = Chunk<E>;
+  constexpr int VEC = G::VEC, LPT = G::LPT, TPI = G::TPI, NI = G::NI;
+  const int r = (threadIdx.x & 63) / LPT;
+  float sc[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) sc[i] = group_sum<LPT>(C::dot(qv, kx[i])) * a.scale_log2;
+  if (tb + BS > ctx) {  // partly filled last block
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const bool dead = tb + i * TPI + r >= ctx;
+      sc[i] = dead ? -INFINITY : sc[i];
+      vx[i] = dead ? make_uint4(0u, 0u, 0u, 0u) : vx[i];
+    }
+  }
+  if (bad) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) sc[i] = __builtin_nanf("");
+  }
+  float mx = m;
+#pragma unroll
+  for (int i = 0; i < NI; ++i) mx = fmaxf(mx, sc[i]);
+  const float alpha = fast_exp2(m - mx);
+  m = mx;
+  l *= alpha;
+#pragma unroll
+  for (int e2 = 0; e2 < VEC; ++e2) acc[e2] *= alpha;
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const float pi = fast_exp2(sc[i] - m);
+    l += pi;
+    float vf[VEC];
+    C::unpack(vx[i], vf);
+#pragma unroll
+    for (int e2 = 0; e2 < VEC; ++e2) acc[e2] = fmaf(pi, vf[e2], acc[e2]);
+  }
+}
+
+// Merge the wave's TPI token rows (lanes c, c + LPT, ... hold the same dims):
+// common maximum, rescaled sums, in a fixed butterfly order.  Every lane ends
+// with the row-merged M, Ls and acc of its dims.
+template <int LPT, int VEC>
+__device__ __forceinline__ void merge_rows(float m, float l, const float (&acc)[VEC], float& M, float& Ls,
+                                           float (&av)[VEC]) {
+  M = m;
+#pragma unroll
+  for (int sft = LPT; sft < 64; sft <<= 1) M = fmaxf(M, __shfl_xor(M, sft, 64));
+  const float f = fast_exp2(m - M);
+  Ls = l * f;
+#pragma unroll
+  for (int e2 = 0; e2 < VEC; ++e2) av[e2] = acc[e2] * f;
+#pragma unroll
+  for (int sft = LPT; sft < 64; sft <<= 1) {
+    Ls += __shfl_xor(Ls, sft, 64);
+#pragma unroll
+    for (int e2 = 0; e2 < VEC; ++e2) av[e2] += __shfl_xor(av[e2], sft, 64);
+  }
+}
+
 // One (sequence, partition) unit of the decode for head h: work-list entry
 // `tagged`.  Called by one wave; lanes as described above.  The partial result
 // goes to slot shared_parts + p of the sequence's slots.
 template <typename E, typename O, int D, int BS>
 __device__ __forceinline__ void private_unit(const DecodeArgs& a, int tagged, int h) {
   using G = DecodeGeom<E, D, BS>;
-  using C = Chunk<E>;
-  constexpr int VEC = G::VEC, LPT = G::LPT, TPI = G::TPI, NI = G::NI;
+  constexpr int VEC = G::VEC, LPT = G::LPT, NI = G::NI;
   const int lane = threadIdx.x & 63;
   const int r = lane / LPT;
   const int c = lane % LPT;
@@ -329,121 +506,26 @@ __device__ __forceinline__ void private_unit(const DecodeArgs& a, int tagged, in
   float acc[VEC];
 #pragma unroll
   for (int e2 = 0; e2 < VEC; ++e2) acc[e2] = 0.f;
-
   auto consume = [&](const uint4 (&kx)[NI], uint4 (&vx)[NI], int jb, bool bad) {
-    const int tb = tok0 + jb * BS;  // position of the block's first token
-    float sc[NI];
-#pragma unroll
-    for (int i = 0; i < NI; ++i) sc[i] = group_sum<LPT>(C::dot(qv, kx[i])) * a.scale_log2;
-    if (tb + BS > ctx) {  // partly filled last block
-#pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        const bool dead = tb + i * TPI + r >= ctx;
-        sc[i] = dead ? -INFINITY : sc[i];
-        vx[i] = dead ? make_uint4(0u, 0u, 0u, 0u) : vx[i];
-      }
-    }
-    if (bad) {
-#pragma unroll
-      for (int i = 0; i < NI; ++i) sc[i] = __builtin_nanf("");
-    }
-    float mx = m;
-#pragma unroll
-    for (int i = 0; i < NI; ++i) mx = fmaxf(mx, sc[i]);
-    const float alpha = fast_exp2(m - mx);
-    m = mx;
-    l *= alpha;
-#pragma unroll
-    for (int e2 = 0; e2 < VEC; ++e2) acc[e2] *= alpha;
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const float pi = fast_exp2(sc[i] - m);
-      l += pi;
-      float vf[VEC];
-      C::unpack(vx[i], vf);
-#pragma unroll
-      for (int e2 = 0; e2 < VEC; ++e2) acc[e2] = fmaf(pi, vf[e2], acc[e2]);
-    }
+    softmax_tile<E, D, BS>(a, qv, kx, vx, tok0 + jb * BS, ctx, bad, m, l, acc);
   };
+  // The stream is instantiated once per load kind, so that the choice is made
+  // once per unit and the loop bodies stay straight-line.
+  if (reuse) stream_tiles<G, false>(a, trow, nblk, kbase, vbase, bstride, consume);
+  else stream_tiles<G, true>(a, trow, nblk, kbase, vbase, bstride, consume);
 
-  // The whole stream is instantiated once per load kind, so that the choice
-  // is made once per unit and the loop bodies stay straight-line.
-  auto run = [&](auto nt_c) {
-    constexpr bool NTL = decltype(nt_c)::value;
-    auto load = [&](int phys, uint4 (&kx)[NI], uint4 (&vx)[NI]) {
-      const char* kp = kbase + (int64_t)phys * bstride;
-      const char* vp = vbase + (int64_t)phys * bstride;
-#pragma unroll
-      for (int i = 0; i < NI; ++i) kx[i] = load_kv16<NTL>(kp + i * 1024);
-#pragma unroll
-      for (int i = 0; i < NI; ++i) vx[i] = load_kv16<NTL>(vp + i * 1024);
-    };
-    for (int cb = 0; cb < nblk; cb += 64) {
-      const int cn = min(64, nblk - cb);
-      // The chunk's table entries, one per lane; a wave-uniform readlane picks each.
-      const int tv = lane < cn ? trow[cb + lane] : 0;
-      auto phys_of = [&](int j, bool& bad) {
-        const int ph = __builtin_amdgcn_readlane(tv, j);
-        bad = (uint64_t)(uint32_t)ph >= (uint64_t)a.num_blocks;
-        return bad ? 0 : ph;
-      };
-      int j = 0;
-      if constexpr (G::PINGPONG) {
-        uint4 kA[NI], vA[NI], kB[NI], vB[NI];
-        bool badA, badB;
-        load(phys_of(j, badA), kA, vA);
-        while (j + 2 < cn) {
-          load(phys_of(j + 1, badB), kB, vB);
-          consume(kA, vA, cb + j, badA);
-          load(phys_of(j + 2, badA), kA, vA);
-          consume(kB, vB, cb + j + 1, badB);
-          j += 2;
-        }
-        if (j + 1 < cn) {
-          load(phys_of(j + 1, badB), kB, vB);
-          consume(kA, vA, cb + j, badA);
-          consume(kB, vB, cb + j + 1, badB);
-        } else {
-          consume(kA, vA, cb + j, badA);
-        }
-      } else {
-        for (; j < cn; ++j) {
-          uint4 kA[NI], vA[NI];
-          bool badA;
-          load(phys_of(j, badA), kA, vA);
-          consume(kA, vA, cb + j, badA);
-        }
-      }
-    }
-  };
-  if (reuse) run(std::false_type{});
-  else run(std::true_type{});
-
-  // Merge the wave's TPI token rows (lanes c, c + LPT, ... hold the same
-  // dims): common maximum, rescaled sums, in a fixed butterfly order.
-  float M = m;
-#pragma unroll
-  for (int sft = LPT; sft < 64; sft <<= 1) M = fmaxf(M, __shfl_xor(M, sft, 64));
-  const float f = fast_exp2(m - M);
-  float Ls = l * f;
-#pragma unroll
-  for (int e2 = 0; e2 < VEC; ++e2) acc[e2] *= f;
-#pragma unroll
-  for (int sft = LPT; sft < 64; sft <<= 1) {
-    Ls += __shfl_xor(Ls, sft, 64);
-#pragma unroll
-    for (int e2 = 0; e2 < VEC; ++e2) acc[e2] += __shfl_xor(acc[e2], sft, 64);
-  }
+  float M, Ls, av[VEC];
+  merge_rows<LPT, VEC>(m, l, acc, M, Ls, av);
   if (r == 0) {
     if (direct) {
 #pragma unroll
-      for (int e2 = 0; e2 < VEC; ++e2) Out<O>::put(a.out, sh * D + c * VEC + e2, acc[e2] / Ls);
+      for (int e2 = 0; e2 < VEC; ++e2) Out<O>::put(a.out, sh * D + c * VEC + e2, av[e2] / Ls);
     } else {
       const int64_t pi = sh * a.num_slots + shared_parts(a, s, part_tokens) + p;
       float* dst = a.ws_acc + pi * D + c * VEC;
 #pragma unroll
       for (int e2 = 0; e2 < VEC; e2 += 4)
-        *reinterpret_cast<float4*>(dst + e2) = make_float4(acc[e2], acc[e2 + 1], acc[e2 + 2], acc[e2 + 3]);
+        *reinterpret_cast<float4*>(dst + e2) = make_float4(av[e2], av[e2 + 1], av[e2 + 2], av[e2 + 3]);
       if (c == 0) *reinterpret_cast<float2*>(a.ws_ml + pi * 2) = make_float2(M, Ls);
     }
   }
@@ -453,8 +535,10 @@ __device__ __forceinline__ void private_unit(const DecodeArgs& a, int tagged, in
 // The wave streams head h of the group's shared blocks once and keeps one
 // online softmax per member (its own query), with the same lane layout as a
 // sequence's own unit.  Every shared block is full and inside every member's
-// context, so no slot is masked.  Each member's partial result goes to its
-// slot p.
+// context, so no slot is masked.  When contexts are not split (P = 1) the unit
+// then streams each member's own remaining blocks with that member's query
+// and writes the members' outputs; otherwise each member's partial result goes
+// to its slot p and its own partitions are units of their own.
 template <typename E, typename O, int D, int BS>
 __device__ __forceinline__ void group_unit(const DecodeArgs& a, int tagged, int h) {
   using G = DecodeGeom<E, D, BS>;
@@ -478,6 +562,7 @@ __device__ __forceinline__ void group_unit(const DecodeArgs& a, int tagged, int 
   if (tok0 >= tend) return;
   const int nblk = (tend - tok0) / BS;
   const int s0 = win * GW;
+  const bool tails = a.num_parts == 1;
 
   uint4 qv[GW];
   float m[GW], l[GW], acc[GW][VEC];
@@ -504,7 +589,7 @@ __device__ __forceinline__ void group_unit(const DecodeArgs& a, int tagged, int 
   // skipped, which keeps the register count, and so the occupancy, where it
   // was.
   constexpr bool ALL_MEMBERS = NI <= 4 && LPT == 16;
-  auto consume = [&](const uint4 (&kx)[NI], const uint4 (&vx)[NI], bool bad) {
+  auto consume = [&](const uint4 (&kx)[NI], const uint4 (&vx)[NI], int, bool bad) {
 #pragma unroll
     for (int g = 0; g < GW; ++g) {
       if constexpr (!ALL_MEMBERS) {
@@ -536,78 +621,38 @@ __device__ __forceinline__ void group_unit(const DecodeArgs& a, int tagged, int 
       }
     }
   };
-  auto load = [&](int phys, uint4 (&kx)[NI], uint4 (&vx)[NI]) {
-    const char* kp = kbase + (int64_t)phys * bstride;
-    const char* vp = vbase + (int64_t)phys * bstride;
-#pragma unroll
-    for (int i = 0; i < NI; ++i) kx[i] = load_kv16<true>(kp + i * 1024);
-#pragma unroll
-    for (int i = 0; i < NI; ++i) vx[i] = load_kv16<true>(vp + i * 1024);
-  };
-  for (int cb = 0; cb < nblk; cb += 64) {
-    const int cn = min(64, nblk - cb);
-    const int tv = lane < cn ? trow[cb + lane] : 0;
-    auto phys_of = [&](int j, bool& bad) {
-      const int ph = __builtin_amdgcn_readlane(tv, j);
-      bad = (uint64_t)(uint32_t)ph >= (uint64_t)a.num_blocks;
-      return bad ? 0 : ph;
-    };
-    int j = 0;
-    if constexpr (G::PINGPONG) {
-      // Two tiles in flight per wave, as in a sequence's own units: with one
-      // wave per SIMD, the second register set keeps the CU's loads in flight.
-      uint4 kA[NI], vA[NI], kB[NI], vB[NI];
-      bool badA, badB;
-      load(phys_of(j, badA), kA, vA);
-      while (j + 2 < cn) {
-        load(phys_of(j + 1, badB), kB, vB);
-        consume(kA, vA, badA);
-        load(phys_of(j + 2, badA), kA, vA);
-        consume(kB, vB, badB);
-        j += 2;
-      }
-      if (j + 1 < cn) {
-        load(phys_of(j + 1, badB), kB, vB);
-        consume(kA, vA, badA);
-        consume(kB, vB, badB);
-      } else {
-        consume(kA, vA, badA);
-      }
-    } else {
-      for (; j < cn; ++j) {
-        uint4 kA[NI], vA[NI];
-        bool badA;
-        load(phys_of(j, badA), kA, vA);
-        consume(kA, vA, badA);
-      }
-    }
-  }
+  stream_tiles<G, true>(a, trow, nblk, kbase, vbase, bstride, consume);
 
-  // Per member: merge the wave's token rows, then store the partial result.
+  // Per member: its own remaining blocks (unsplit contexts), then the merge
+  // of the wave's token rows and the store.
 #pragma unroll
   for (int g = 0; g < GW; ++g) {
     if (!((mask >> g) & 1)) continue;
-    float M = m[g];
-#pragma unroll
-    for (int sft = LPT; sft < 64; sft <<= 1) M = fmaxf(M, __shfl_xor(M, sft, 64));
-    const float f = fast_exp2(m[g] - M);
-    float Ls = l[g] * f;
-    float av[VEC];
-#pragma unroll
-    for (int e2 = 0; e2 < VEC; ++e2) av[e2] = acc[g][e2] * f;
-#pragma unroll
-    for (int sft = LPT; sft < 64; sft <<= 1) {
-      Ls += __shfl_xor(Ls, sft, 64);
-#pragma unroll
-      for (int e2 = 0; e2 < VEC; ++e2) av[e2] += __shfl_xor(av[e2], sft, 64);
+    const int s = s0 + g;
+    const int64_t sh = (int64_t)s * H + h;
+    if (tails) {
+      const int ctx = clamp_ctx(a, s);
+      const int own = (ctx + BS - 1) / BS - J;  // blocks past the shared ones
+      const int32_t* orow = a.block_tables + (int64_t)s * a.max_blocks_per_seq + J;
+      auto consume1 = [&](const uint4 (&kx)[NI], uint4 (&vx)[NI], int jb, bool bad) {
+        softmax_tile<E, D, BS>(a, qv[g], kx, vx, (J + jb) * BS, ctx, bad, m[g], l[g], acc[g]);
+      };
+      if (own > 0) stream_tiles<G, true>(a, orow, own, kbase, vbase, bstride, consume1);
     }
+    float M, Ls, av[VEC];
+    merge_rows<LPT, VEC>(m[g], l[g], acc[g], M, Ls, av);
     if (r == 0) {
-      const int64_t pi = ((int64_t)(s0 + g) * H + h) * a.num_slots + p;
-      float* dst = a.ws_acc + pi * D + c * VEC;
+      if (tails) {
 #pragma unroll
-      for (int e2 = 0; e2 < VEC; e2 += 4)
-        *reinterpret_cast<float4*>(dst + e2) = make_float4(av[e2], av[e2 + 1], av[e2 + 2], av[e2 + 3]);
-      if (c == 0) *reinterpret_cast<float2*>(a.ws_ml + pi * 2) = make_float2(M, Ls);
+        for (int e2 = 0; e2 < VEC; ++e2) Out<O>::put(a.out, sh * D + c * VEC + e2, av[e2] / Ls);
+      } else {
+        const int64_t pi = sh * a.num_slots + p;
+        float* dst = a.ws_acc + pi * D + c * VEC;
+#pragma unroll
+        for (int e2 = 0; e2 < VEC; e2 += 4)
+          *reinterpret_cast<float4*>(dst + e2) = make_float4(av[e2], av[e2 + 1], av[e2 + 2], av[e2 + 3]);
+        if (c == 0) *reinterpret_cast<float2*>(a.ws_ml + pi * 2) = make_float2(M, Ls);
+      }
     }
   }
 }
@@ -728,8 +773,6 @@ static int decode_wg_per_cu() {
 
 template <typename E, typename O, int D, int BS>
 static hipError_t partial_bs(const DecodeArgs& a, hipStream_t st) {
-  if (a.win_info != nullptr)
-    hipLaunchKernelGGL(share_detect_kernel, dim3((a.num_windows + 15) / 16), dim3(1024), 0, st, a);
   hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(1024), 0, st, a);
   // One workgroup per CU: one wave per SIMD, two tiles in flight per wave.
   // On MI355X this streams the gathered tiles faster than running the

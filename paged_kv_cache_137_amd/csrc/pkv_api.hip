@@ -140,9 +140,9 @@ int32_t resolve_partition(int32_t partition_size, int32_t num_seqs, int32_t num_
   return (int32_t)size;
 }
 
-// stages: kBoth is the one-call decode (sharing found on the device, then
-// plan, decode and reduce); kPartial and kReduce are the two stages of the
-// two-stage form (no sharing; the reduce runs only for split contexts).
+// stages: kBoth is the one-call decode (sharing found on the device by the
+// plan kernel); kPartial and kReduce are the two stages of the two-stage form
+// (no sharing).  The reduce runs only for split contexts.
 int decode_impl(int stages, const void* q, const void* k_cache, const void* v_cache, const pkv_cache_desc* desc,
                 const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
                 int32_t num_seqs, int32_t max_context_len, float scale, void* out, int32_t out_dtype,
@@ -221,9 +221,9 @@ int decode_impl(int stages, const void* q, const void* k_cache, const void* v_ca
     st = launch_status(pkv::launch_decode_partial(a, desc->dtype, out_dtype, desc->head_dim, sm));
     if (st != PKV_OK) return st;
   }
-  // The one-call decode merges whenever a sequence may have more than one
-  // partial result: split contexts, or a sharing group (found on the device).
-  if ((stages & kReduce) && (one_call || plan.num_parts > 1)) {
+  // Only split contexts leave partial results to merge: with P = 1 a sharing
+  // group's unit also streams its members' own blocks and writes their outputs.
+  if ((stages & kReduce) && plan.num_parts > 1) {
     st = launch_status(pkv::launch_decode_reduce(a, out_dtype, desc->head_dim, sm));
     if (st != PKV_OK) return st;
   }
