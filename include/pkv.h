@@ -307,6 +307,30 @@ int pkv_paged_attn_decode_shared(const void* q, const void* k_cache, const void*
                                  void* stream);
 
 /*
+ * pkv_kv_read_probe - the decode's K/V reads without its arithmetic; a
+ * measurement aid, not part of the attention path.
+ *
+ * Reads exactly the (block, head) tiles that the two-stage decode reads for
+ * the same arguments (every block 0 .. ceil(context_lens[s] / block_size) - 1
+ * of every sequence, keys and values, whole tiles), with the same plan,
+ * persistent scheduling and nontemporal 16-byte loads ("vLLM & PagedAttention
+ * ...", section III: blocks gathered through the block table), and computes no
+ * attention.  Its time is the HBM rate of the decode's access pattern alone,
+ * the ceiling the decode can approach; it also calibrates hardware byte
+ * counters for these loads.
+ *   out    uint32 [num_seqs][num_heads], all zero on entry (the caller
+ *          clears it); receives the XOR of every 32-bit word of the
+ *          sequence's K and V tiles for that head.
+ * Other arguments, preconditions and errors as for the two-stage decode; the
+ * workspace is sized by pkv_decode_workspace_bytes.  A table entry outside the
+ * pool is not read and contributes nothing.
+ */
+int pkv_kv_read_probe(const void* k_cache, const void* v_cache, const pkv_cache_desc* desc,
+                      const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                      int32_t num_seqs, int32_t max_context_len, int32_t partition_size, uint32_t* out,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * pkv_paged_attn_prefill - causal self-attention over each prompt (prompt phase).
  *
  * All positions of a prompt are known at once, so this is dense matrix-matrix

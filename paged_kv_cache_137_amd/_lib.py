@@ -37,6 +37,7 @@ SIGNATURES = {
     "pkv_paged_attn_decode_noalloc": ([_vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _f32, _vp, _i32, _i32, _vp],
                                       ctypes.c_int),
     "pkv_copy_blocks": ([_vp, _vp, _vp, _vp, _i64, _vp], ctypes.c_int),
+    "pkv_kv_read_probe": ([_vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _vp, _vp, _sz, _vp], ctypes.c_int),
     "pkv_swap_blocks": ([_vp, _vp, _i64, _vp, _vp, _i64, _vp, _vp, _i64, _vp], ctypes.c_int),
     "pkv_paged_attn_prefill_cached": (
         [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32, _i64, _i32, _i32, _f32, _vp, _i32, _vp],

@@ -739,6 +739,54 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const DecodeArgs a) {
   }
 }
 
+// Read probe: the decode's tile reads without its arithmetic.  The same plan,
+// units, scheduling and loads as the two-stage decode; each wave folds every
+// 32-bit word of the K and V tiles it reads (whole tiles, the slots past the
+// context included) with XOR, and out[s][h] receives the fold over the
+// sequence's blocks 0 .. ceil(ctx / BS) - 1 (XOR of the units' folds).  It
+// measures how fast this access pattern streams from HBM.
+template <typename E, int D, int BS>
+__global__ __launch_bounds__(NW * 64) void read_probe_kernel(const DecodeArgs a, uint32_t* out) {
+  using G = DecodeGeom<E, D, BS>;
+  constexpr int NI = G::NI;
+  __shared__ int sm_unit[2];
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int H = a.num_heads;
+  const int HG = (H + NW - 1) / NW;
+  const int64_t bstride = (int64_t)H * G::TILE;
+  const int part_tokens = a.part_blocks * BS;
+  const int total = a.work_ctrl[1] * HG;
+  for (int it = 0;; ++it) {
+    if (threadIdx.x == 0) sm_unit[it & 1] = atomicAdd(&a.work_ctrl[0], 1);
+    __syncthreads();
+    const int u = __builtin_amdgcn_readfirstlane(sm_unit[it & 1]);
+    if (u >= total) break;
+    const int e = u / HG;
+    const int h = (u - e * HG) * NW + w;
+    if (h >= H) continue;
+    const int entry = __builtin_amdgcn_readfirstlane(a.work_list[e]) >> ENTRY_SHIFT;
+    const int s = entry / a.num_parts;
+    const int p = entry - s * a.num_parts;
+    const int ctx = clamp_ctx(a, s);
+    const int tok0 = p * part_tokens;
+    if (ctx <= 0 || tok0 >= ctx) continue;
+    const int nblk = (min(part_tokens, ctx - tok0) + BS - 1) / BS;
+    const char* kbase = reinterpret_cast<const char*>(a.k_cache) + (int64_t)h * G::TILE + lane * 16;
+    const char* vbase = reinterpret_cast<const char*>(a.v_cache) + (int64_t)h * G::TILE + lane * 16;
+    const int32_t* trow = a.block_tables + (int64_t)s * a.max_blocks_per_seq + tok0 / BS;
+    uint32_t x = 0;
+    auto consume = [&](const uint4 (&kx)[NI], const uint4 (&vx)[NI], int, bool) {
+#pragma unroll
+      for (int i = 0; i < NI; ++i) x ^= kx[i].x ^ kx[i].y ^ kx[i].z ^ kx[i].w ^ vx[i].x ^ vx[i].y ^ vx[i].z ^ vx[i].w;
+    };
+    stream_tiles<G, true>(a, trow, nblk, kbase, vbase, bstride, consume);
+#pragma unroll
+    for (int sft = 1; sft < 64; sft <<= 1) x ^= (uint32_t)__shfl_xor((int)x, sft, 64);
+    if (lane == 0) atomicXor(out + (int64_t)s * H + h, x);
+  }
+}
+
 // Workgroups of a persistent kernel: per_cu on every CU of the device (at
 // most the kernel's occupancy), never more than there are units.  The CU
 // count and the occupancy are cached per kernel and device.
@@ -802,6 +850,28 @@ template <typename E, int D>
 static hipError_t partial_out(const DecodeArgs& a, int out_dtype, hipStream_t st) {
   if (out_dtype == 0) return partial_t<E, f32_t, D>(a, st);
   return partial_t<E, E, D>(a, st);
+}
+
+template <typename E, int D, int BS>
+static hipError_t probe_bs(const DecodeArgs& a, uint32_t* out, hipStream_t st) {
+  hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(1024), 0, st, a);
+  const int64_t units = (int64_t)a.max_entries * ((a.num_heads + NW - 1) / NW);
+  const int grid = persistent_grid<read_probe_kernel<E, D, BS>>(NW * 64, units, 1);
+  hipLaunchKernelGGL((read_probe_kernel<E, D, BS>), dim3(grid), dim3(NW * 64), 0, st, a, out);
+  return hipGetLastError();
+}
+
+template <typename E, int D>
+static hipError_t probe_d(const DecodeArgs& a, uint32_t* out, hipStream_t st) {
+  if (a.block_size == 8) return probe_bs<E, D, 8>(a, out, st);
+  if (a.block_size == 32) return probe_bs<E, D, 32>(a, out, st);
+  return probe_bs<E, D, 16>(a, out, st);
+}
+
+hipError_t launch_read_probe(const DecodeArgs& a, int dtype, int head_dim, uint32_t* out, hipStream_t st) {
+  // Only the element size matters to the loads: fp16 and bf16 share the 16-bit geometry.
+  if (head_dim == 128) return dtype == 0 ? probe_d<f32_t, 128>(a, out, st) : probe_d<f16_t, 128>(a, out, st);
+  return dtype == 0 ? probe_d<f32_t, 64>(a, out, st) : probe_d<f16_t, 64>(a, out, st);
 }
 
 // dtype codes follow pkv_dtype: 0 = f32, 1 = f16, 2 = bf16.

@@ -419,6 +419,52 @@ int pkv_paged_attn_decode_noalloc(const void* q, const void* k_cache, const void
                      num_seqs, max_context_len, scale, out, out_dtype, part, ws, PKV_NOALLOC_SCRATCH_BYTES, stream);
 }
 
+int pkv_kv_read_probe(const void* k_cache, const void* v_cache, const pkv_cache_desc* desc,
+                      const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                      int32_t num_seqs, int32_t max_context_len, int32_t partition_size, uint32_t* out,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_desc(desc);
+  if (st != PKV_OK) return st;
+  if (num_seqs < 0 || max_blocks_per_seq <= 0 || max_context_len <= 0) return PKV_EINVAL;
+  const int32_t bsz = desc->block_size;
+  if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * bsz) return PKV_EINVAL;
+  partition_size = resolve_partition(partition_size, num_seqs, desc->num_heads, max_context_len, false);
+  if (partition_size != 0 && (partition_size % bsz != 0 || partition_size < 16 || partition_size > 4096))
+    return PKV_EINVAL;
+  if (num_seqs == 0) return PKV_OK;
+  if (!k_cache || !v_cache || !block_tables || !context_lens || !out || !workspace) return PKV_EINVAL;
+  if (!aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 4) || !aligned(workspace, 16) ||
+      !aligned(block_tables, 4) || !aligned(context_lens, 4))
+    return PKV_EINVAL;
+  if (desc->num_heads > 65535 || num_seqs > (1 << 24)) return PKV_EINVAL;
+  const DecodePlan plan = plan_decode(num_seqs, desc->num_heads, desc->head_dim, max_context_len, partition_size, bsz);
+  const int64_t groups = (desc->num_heads + kHeadsPerUnit - 1) / kHeadsPerUnit;
+  if (plan.max_entries >= ((int64_t)1 << 29) || plan.max_entries * groups > ((int64_t)1 << 31) - 64)
+    return PKV_EINVAL;
+  if (workspace_bytes < plan.ws_bytes) return PKV_EWORKSPACE;
+  st = device_status();
+  if (st != PKV_OK) return st;
+  pkv::DecodeArgs a{};
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  char* ws = reinterpret_cast<char*>(workspace);
+  a.work_ctrl = reinterpret_cast<int32_t*>(ws);
+  a.work_list = reinterpret_cast<int32_t*>(ws + plan.list_off);
+  a.num_blocks = desc->num_blocks;
+  a.num_heads = desc->num_heads;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.num_seqs = num_seqs;
+  a.max_context_len = max_context_len;
+  a.block_size = bsz;
+  a.part_blocks = plan.part_blocks;
+  a.num_parts = plan.num_parts;
+  a.num_slots = plan.num_parts + 1;
+  a.max_entries = num_seqs * plan.num_parts;
+  return launch_status(pkv::launch_read_probe(a, desc->dtype, desc->head_dim, out, reinterpret_cast<hipStream_t>(stream)));
+}
+
 int pkv_paged_attn_decode_partial(const void* q, const void* k_cache, const void* v_cache,
                                   const pkv_cache_desc* desc, const int32_t* block_tables,
                                   int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,

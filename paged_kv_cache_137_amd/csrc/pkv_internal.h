@@ -100,6 +100,8 @@ hipError_t launch_kv_cache_write(const WriteArgs& a, hipStream_t stream);
 // kernels; then the reduce, which merges partial results.
 hipError_t launch_decode_partial(const DecodeArgs& a, int dtype, int out_dtype, int head_dim, hipStream_t stream);
 hipError_t launch_decode_reduce(const DecodeArgs& a, int out_dtype, int head_dim, hipStream_t stream);
+// The decode's tile reads without its arithmetic (pkv_kv_read_probe).
+hipError_t launch_read_probe(const DecodeArgs& a, int dtype, int head_dim, uint32_t* out, hipStream_t stream);
 
 // Sequences per sharing window of the decode (a group has at most this many
 // members).

@@ -258,6 +258,39 @@ def paged_attn_decode_reduce(q, k_cache, v_cache, block_tables, context_lens, sc
                         out, max_context_len, partition_size, workspace)
 
 
+def kv_read_probe(k_cache, v_cache, block_tables, context_lens, out=None, *, max_context_len: int | None = None,
+                  partition_size: int = DEFAULT_PARTITION, workspace: torch.Tensor | None = None):
+    """The decode's K/V tile reads without its arithmetic (a measurement aid).
+
+    Returns out, uint32 [S][H] as int32 storage: the XOR of every 32-bit word of
+    each sequence's K and V tiles for that head, over blocks 0 .. ceil(ctx/B)-1.
+    """
+    _need(k_cache, "k_cache", dim=4)
+    dev = k_cache.device
+    _need(v_cache, "v_cache", dtype=k_cache.dtype, device=dev)
+    _need(block_tables, "block_tables", dtype=torch.int32, dim=2, device=dev)
+    _need(context_lens, "context_lens", dtype=torch.int32, dim=1, device=dev)
+    S, H = context_lens.shape[0], k_cache.shape[1]
+    if out is None:
+        out = torch.zeros((S, H), dtype=torch.int32, device=dev)
+    else:
+        _need(out, "out", dtype=torch.int32, dim=2, device=dev)
+        out.zero_()
+    mbps = block_tables.shape[1]
+    if max_context_len is None:
+        max_context_len = mbps * k_cache.shape[2]
+    need = decode_workspace_bytes(S, H, k_cache.shape[3], max_context_len, partition_size) if S else 0
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    desc = cache_desc(k_cache)
+    with torch.cuda.device(dev):
+        check("pkv_kv_read_probe", lib().pkv_kv_read_probe(
+            _ptr(k_cache), _ptr(v_cache), ctypes.byref(desc), _ptr(block_tables), mbps, _ptr(context_lens), S,
+            int(max_context_len), int(partition_size), _ptr(out), _ptr(workspace), ws_bytes, _stream(dev)))
+    return out
+
+
 def paged_attn_prefill(q, k, v, block_tables, prompt_lens, out, *, scale: float | None = None,
                        max_prompt_len: int | None = None):
     """Causal attention of packed prompts q/k/v [T][H][D] (f16 or bf16); fills out.

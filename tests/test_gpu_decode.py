@@ -420,3 +420,26 @@ def test_block_size_variants(bs, dt, D):
     ops.copy_blocks(t["k_cache"], t["v_cache"], up(pairs))
     ek, ev = oracle.attention.copy_blocks(kc, vc, pairs)
     assert np.array_equal(bits(down(t["k_cache"])), bits(ek)) and np.array_equal(bits(down(t["v_cache"])), bits(ev))
+
+
+@pytest.mark.parametrize("dt,D,B", [("bf16", 128, 16), ("f32", 64, 8), ("f16", 128, 32)])
+def test_read_probe_reads_every_tile_of_every_context(dt, D, B):
+    """The read probe (the decode's loads without its arithmetic) folds exactly
+    the tiles a decode reads: blocks 0 .. ceil(ctx/B)-1 of every sequence, keys
+    and values, whole tiles.  Its XOR per (sequence, head) equals one computed
+    on the host from the same pool, bit for bit, split or not."""
+    print(f"read probe {dt} D={D} B={B}", flush=True)
+    lens = [1, 17, B, B + 1, 300, 1000, 2049]
+    d = W.make_decode(77, dt, 4, D, lens, block_size=B)
+    t = upload_decode(d)
+    u32 = lambda x: np.ascontiguousarray(x).view(np.uint32)  # noqa: E731
+    want = np.zeros((d.num_seqs, 4), np.uint32)
+    for s, n in enumerate(lens):
+        blocks = d.block_tables[s, : -(-n // B)]
+        for h in range(4):
+            want[s, h] = np.bitwise_xor.reduce(
+                np.concatenate([u32(d.k_cache[blocks, h]).ravel(), u32(d.v_cache[blocks, h]).ravel()]))
+    for part in (0, 512, ops.PARTITION_AUTO):
+        got = ops.kv_read_probe(t["k_cache"], t["v_cache"], t["block_tables"], t["context_lens"],
+                                max_context_len=d.max_context_len, partition_size=part)
+        assert np.array_equal(got.cpu().numpy().view(np.uint32), want), part
