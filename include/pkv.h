@@ -418,9 +418,9 @@ int pkv_copy_blocks(void* k_cache, void* v_cache, const pkv_cache_desc* desc, co
  * When memory runs out, a preempted sequence's blocks are evicted all
  * together.  With swapping, they are copied to a pool in CPU memory and
  * brought back later, possibly into different physical blocks ("vLLM &
- * PagedAttention ...", section VIII; P1 section 4.5).  This call copies the
- * (source block, destination block) pairs from one pool to another, all
- * heads, keys and values, in one launch.  Either pool may be device memory or
+ * PagedAttention ...", section VIII; "PagedAttention and vLLM, annotated",
+ * section 4.5).  This call copies the (source block, destination block)
+ * pairs from one pool to another, all heads, keys and values, in one launch.  Either pool may be device memory or
  * pinned host memory (hipHostMalloc, or torch's pin_memory); the GPU reads or
  * writes host memory directly over the bus.
  *

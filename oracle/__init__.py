@@ -6,9 +6,10 @@ package.  The product path (the HIP library and its Python binding) never calls
 it and never falls back to it.  It shares no code with that path.  It is written
 directly from the pages' definitions, in float64, with no blocking or fusion.
 
-Sources (the pages this reproduces):
-  P1  "PagedAttention and vLLM, annotated"
-  P3  "vLLM & PagedAttention: Efficient Memory Management for LLM Serving"
+Sources (the pages this reproduces), cited by title and section:
+  "PagedAttention and vLLM, annotated"
+  "vLLM & PagedAttention: Efficient Memory Management for LLM Serving"
+  (shortened to "vLLM & PagedAttention" after the first mention in a file)
 
 Modules:
   bookkeeping  block counts, slot numbering, per-token KV bytes (integer, exact)

@@ -2,17 +2,18 @@
 
 TEST INFRASTRUCTURE ONLY: the oracle, never the product path.
 
-What is computed is plain softmax attention.  P3 ("vLLM & PagedAttention:
-Efficient Memory Management for LLM Serving"), section I, attention equation:
+What is computed is plain softmax attention: the attention equation of "vLLM &
+PagedAttention: Efficient Memory Management for LLM Serving", section I,
     a_ij = exp(q_i . k_j / sqrt(d)) / sum_{t <= i} exp(q_i . k_t / sqrt(d)),
     o_i  = sum_{j <= i} a_ij v_j.
-P1 ("PagedAttention and vLLM, annotated"), section 4.1, says the paged,
+"PagedAttention and vLLM, annotated", section 4.1, says the paged,
 block-by-block evaluation gives exactly this value.  It is the same as attending
 over one contiguous array.  So the oracle first reassembles each sequence's
-contiguous K and V from its block list (P3 section III, the block-wise equation
-and the logical/physical blocks).  Slots at or past the context length are
-dropped: the partly filled last block of P1 section 4.1.  Then it applies the
-equation above, with no blocking, tiling or online rescaling.
+contiguous K and V from its block list (the block-wise equation and the
+logical/physical blocks of "vLLM & PagedAttention", section III).  Slots at or
+past the context length are dropped: the partly filled last block of section
+4.1 of the annotated page.  Then it applies the equation above, with no
+blocking, tiling or online rescaling.
 
 Layouts (the same as the GPU path's, because both read the same input bytes):
     cache  [num_blocks][num_heads][block_size][head_dim]
@@ -42,8 +43,8 @@ def cache_write(k_cache, v_cache, k, v, slot_mapping, block_size: int):
     For every token t with slot_mapping[t] >= 0, and every head h:
         cache[slot // B][h][slot % B][:] = new[t][h][:]
     The copy is byte-for-byte, with no conversion.  Every other byte of the pool is
-    unchanged.  A negative slot marks a padding token and is skipped.  P3 section X
-    describes this step as a fused reshape-and-block-write of the new KV into the
+    unchanged.  A negative slot marks a padding token and is skipped.
+    "vLLM & PagedAttention", section X, describes this step as a fused reshape-and-block-write of the new KV into the
     block-table positions.  Section V of the same page gives the order: prompt
     tokens fill logical blocks left to right, and a decode token goes to the next
     free slot.
@@ -69,8 +70,9 @@ def copy_blocks(k_cache, v_cache, block_pairs):
 
     For each (src, dst) pair, cache[dst] = cache[src], byte for byte.  This is the
     copy-on-write step: a write into a shared block copies the block first, and
-    the writer moves to the copy (P3 section VII, Figure 8).  All copies of a step
-    are batched into one launch (P3 section X).  Pairs are applied in order.
+    the writer moves to the copy ("vLLM & PagedAttention", section VII, Figure
+    8).  All copies of a step are batched into one launch (section X of the same
+    page).  Pairs are applied in order.
     """
     kc, vc = k_cache.copy(), v_cache.copy()
     ut = _UINT[kc.dtype.itemsize]
@@ -87,7 +89,8 @@ def copy_blocks(k_cache, v_cache, block_pairs):
 def gather(cache: np.ndarray, block_table, context_len: int, block_size: int) -> np.ndarray:
     """A sequence's contiguous [num_heads][context_len][head_dim] view, built block by block.
 
-    Logical block j lives in physical block block_table[j] (P1 section 4.2).
+    Logical block j lives in physical block block_table[j] ("PagedAttention and
+    vLLM, annotated", section 4.2).
     Blocks are concatenated in logical order.  Rows at or past context_len are dropped.
     """
     nb = -(-context_len // block_size)
@@ -129,8 +132,8 @@ def causal_prefill(q, k, v, prompt_lens, scale: float, dtype: str, prompts=None)
     """Causal self-attention of each packed prompt; float64 [T][H][D].
 
     Row i of a prompt attends to rows 0..i of the same prompt: the t <= i limit of
-    the attention equation in P3 section I.  The prompt phase computes all positions
-    at once.  `prompts` restricts the work to some prompts.  Rows of the others stay NaN.
+    the attention equation in "vLLM & PagedAttention", section I.  The prompt
+    phase computes all positions at once.  `prompts` restricts the work to some prompts.  Rows of the others stay NaN.
     """
     T, H, D = q.shape
     out = np.full((T, H, D), np.nan)
@@ -158,11 +161,12 @@ def prefix_prefill(q, k_cache, v_cache, block_tables, prefix_lens, prompt_lens, 
     """Prompt-phase attention of new tokens over a cached prefix plus themselves; float64 [T][H][D].
 
     Prompt p already has prefix_lens[p] tokens in the pool (the cached shared
-    prefix of P3 section VII), followed by its prompt_lens[p] new tokens, whose
+    prefix of "vLLM & PagedAttention", section VII), followed by its
+    prompt_lens[p] new tokens, whose
     K/V are in the pool too.  All of them are read through the prompt's block
     table.  New token i sits at position prefix_lens[p] + i.  It attends to
-    positions 0 .. prefix_lens[p] + i, the t <= i limit of P3 section I's
-    equation.  Compute runs only over the new tokens.  q and the output hold the
+    positions 0 .. prefix_lens[p] + i, the t <= i limit of the equation in
+    section I of the same page.  Compute runs only over the new tokens.  q and the output hold the
     new tokens only, packed prompt after prompt.
     """
     T, H, D = q.shape

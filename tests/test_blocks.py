@@ -118,8 +118,8 @@ def test_sharing_config_accounting():
 
 
 def test_figure9_beam_prune_and_regrow():
-    # P3 section VII, Figure 9 prints only the block ids: all four candidates
-    # share prompt block 0; pruning frees 2, 4, 5 and 8; survivors get 9-12.  This
+    # "vLLM & PagedAttention", section VII, Figure 9 prints only the block ids:
+    # all four candidates share prompt block 0; pruning frees 2, 4, 5 and 8; survivors get 9-12.  This
     # history (block size 4, free list in increasing order) is one tree that is
     # consistent with those ids.
     g = GOLD["figure9"]

@@ -69,7 +69,8 @@ def test_block_table_figure():
     assert BK.blocks_needed(tokens, B) == nb
     assert BK.wasted_slots(tokens, B) == g["empty_slots"]
     assert BK.filled_counts(tokens, B)[-1] == B - g["empty_slots"]
-    # Waste stays below one block for every length (P1 section 4.2, P3 section III).
+    # Waste stays below one block for every length ("PagedAttention and vLLM,
+    # annotated", section 4.2; "vLLM & PagedAttention", section III).
     for n in range(1, 200):
         assert 0 <= BK.wasted_slots(n, B) < B
 
@@ -464,7 +465,8 @@ def test_prefix_prefill_reduces_to_causal_and_to_decode():
 
 
 def test_block_count_invariants():
-    # Closed forms every block size must satisfy (P1 section 4.2; P3 section III):
+    # Closed forms every block size must satisfy ("PagedAttention and vLLM,
+    # annotated", section 4.2; "vLLM & PagedAttention", section III):
     # the blocks hold the tokens with less than one block to spare, and the last
     # block is full exactly when the length is a multiple of the block size.
     for B in (1, 4, 8, 16, 32):
