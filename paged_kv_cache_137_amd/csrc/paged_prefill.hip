@@ -56,12 +56,6 @@
 
 namespace pkv {
 
-// Build-time alternative for measuring the XCD-aware work-item mapping:
-// PKV_PRE_XCD=0 maps workgroup i to item i.
-#ifndef PKV_PRE_XCD
-#define PKV_PRE_XCD 1
-#endif
-
 // Buffer resource word 3 for gfx9-family parts: raw (untyped) 32-bit dword access.
 constexpr int BUF_RSRC_WORD3 = 0x00020000;
 
