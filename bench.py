@@ -19,8 +19,10 @@ The same line also carries:
                 mean duration from HIP events on the launch stream, against
                 MI355X's 8 TB/s.  traffic comes from the committed rocprofv3
                 counter summary, if it was taken on this kernel source.
-  cpu_baseline  the float64 CPU oracle, one thread, on a time-boxed sample of
-                the same step's sequences.
+  cpu_baseline  the float64 CPU oracle as it stands, on the host's cores (one
+                process per core) and on one thread, over a time-boxed sample
+                of the same step's sequences; and its prefill on config 5's
+                prompts.
   mixed_step    the mixed prefill+decode step (8 prompts prefilled while 192
                 sequences decode), per kernel, with prefill's MFMA rate; and
                 the same step with the prefill on a second stream beside the
@@ -31,6 +33,8 @@ The same line also carries:
                 through paged_attn_decode (which reads shared blocks once) and
                 through the two-stage form (which does not).
   cached_prefix_prefill  requests prefilling over one cached shared prefix.
+  prefill_prompt_count  the fresh prefill alone on config 5's 8 prompts and on
+                256 prompts of the same length distribution.
   block_size_sweep  the same decode at 8-, 16- and 32-token blocks (the pool's
                 bytes re-tiled, fresh shuffled tables).
   decode_launch_shape  the headline decode at 1, 2 and 4 workgroups per CU.
@@ -258,6 +262,7 @@ def main() -> int:
         line["opt13b_decode"] = opt13b_decode(a, dev, up)
         line["sharing_step"] = sharing_step(a, dev, up)
         line["cached_prefix_prefill"] = cached_prefix_prefill(a, dev, up)
+        line["prefill_prompt_count"] = prefill_prompt_count(a, dev, up)
 
     if cpu_line is not None:
         line["cpu_baseline"] = cpu_line
@@ -592,6 +597,46 @@ def cached_prefix_prefill(a, dev, up):
         "TFLOPs": round(flops / (ms * 1e-3) / 1e12, 1),
         "mfma_frac": round(flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
     }
+
+
+def prefill_prompt_count(a, dev, up):
+    """The fresh prefill alone (HIP events, inputs resident and warm): config 5's
+    8 prompts, and 256 prompts drawn from the same length distribution
+    (U[128, 2048]), which take the enumeration for more than 64 prompts.  Both
+    32 heads x 128, bf16.  q/k/v of the 256-prompt batch are drawn on the device
+    (seeded); only the timing is used."""
+    import numpy as np
+    import torch
+
+    from paged_kv_cache_137_amd import ops
+    from paged_kv_cache_137_amd import workloads as W
+
+    H, D = 32, 128
+    res = {"workload": "fresh causal prefill alone, 32 heads x 128, bf16: config 5's 8 prompts, and 256 prompts "
+                       "with lengths U[128, 2048]"}
+    p5 = W.mixed_config(poison=False).prefill
+    g = torch.Generator(device=dev)
+    g.manual_seed(137256)
+    cases = (("8_prompts", p5.prompt_lens.astype(np.int64), True),
+             ("256_prompts", np.random.default_rng(137256).integers(128, 2049, size=256).astype(np.int64), False))
+    for name, L, from_workload in cases:
+        T = int(L.sum())
+        if from_workload:
+            q, k, v = up(p5.q, "bf16"), up(p5.k, "bf16"), up(p5.v, "bf16")
+        else:
+            q, k, v = (torch.randn((T, H, D), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+                       for _ in range(3))
+        out = torch.empty((T, H, D), dtype=torch.bfloat16, device=dev)
+        lens = up(L.astype(np.int32))
+        steps = a.steps if T < 20000 else max(3, a.steps // 10)
+        ms = _time_events(lambda: ops.paged_attn_prefill(q, k, v, None, lens, out, max_prompt_len=int(L.max())),
+                          max(1, a.warmup // 2), steps)
+        flops = 4.0 * D * H * float((L * (L + 1) // 2).sum())
+        res[name] = {"tokens": T, "ms": round(ms, 4), "TFLOPs": round(flops / (ms * 1e-3) / 1e12, 1),
+                     "mfma_frac": round(flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
+        del q, k, v, out
+    res["tflops_256_over_8"] = round(res["256_prompts"]["TFLOPs"] / res["8_prompts"]["TFLOPs"], 4)
+    return res
 
 
 def decode_launch_shape(a, t, d, dargs, dkw):

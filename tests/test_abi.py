@@ -133,6 +133,23 @@ def test_auto_partition(lib):
     assert lib.pkv_decode_partition(4, 8, 100, auto, 0, None) == _lib.PKV_EINVAL
 
 
+def test_auto_partition_reads_max_context_len(lib):
+    """The shape rule sees max_context_len, not the lengths: a 1,024-unit batch
+    whose tables are padded to 8,192 tokens is split when the capacity is passed,
+    and left whole when the real maximum is; the per-batch rule reads the
+    lengths themselves and leaves it whole."""
+    import ctypes as C
+
+    auto = _lib.PKV_PARTITION_AUTO
+    assert _part(lib, 256, 16, 8192, auto, 0) == 2048
+    assert _part(lib, 256, 16, 300, auto, 0) == 0
+    lens = [1 + (53 * i) % 300 for i in range(256)]
+    arr = (C.c_int32 * len(lens))(*lens)
+    out = C.c_int32(-1)
+    assert lib.pkv_decode_partition_for_lengths(arr, len(lens), 16, C.byref(out)) == _lib.PKV_OK
+    assert out.value == 0
+
+
 def test_partition_for_lengths(lib):
     import ctypes as C
 

@@ -179,6 +179,33 @@ def test_decode_auto_partition_bounds_long_contexts():
     assert torch.equal(auto, run_decode(ops, t, d, "f32", partition_size=2048))
 
 
+def test_decode_padded_tables_auto_partition():
+    """Tables padded far past the contexts (512 blocks, 8,192 tokens, for
+    contexts of at most 300).  The automatic rule reads max_context_len: left at
+    the table capacity it splits this 1,024-unit batch into 2,048-token
+    partitions; given the real maximum it does not split.  Both decode every
+    sequence to the oracle's values; the real-maximum call equals the explicit
+    no-split call bit for bit."""
+    print("decode, padded tables, automatic partition", flush=True)
+    lens = [1 + (53 * i) % 300 for i in range(256)]
+    d = _batch(77, "bf16", lens, H=16)
+    S, H = d.num_seqs, 16
+    tables = np.pad(d.block_tables, ((0, 0), (0, 512 - d.block_tables.shape[1])), constant_values=d.pad_block)
+    assert ops.decode_partition(S, H, 512 * 16) == 2048
+    assert ops.decode_partition(S, H, max(lens)) == 0
+    t = upload_decode(d)
+    tb = up(tables, None)
+    outs = {}
+    for name, mcl, part in (("capacity", None, ops.PARTITION_AUTO), ("real", max(lens), ops.PARTITION_AUTO),
+                            ("explicit", max(lens), 0)):
+        out = nan_out((S, H, 128), "f32")
+        ops.paged_attn_decode(t["q"], t["k_cache"], t["v_cache"], tb, t["context_lens"], d.scale, out,
+                              max_context_len=mcl, partition_size=part)
+        _check(d, out, None, list(range(S)))
+        outs[name] = out
+    assert torch.equal(outs["real"], outs["explicit"])
+
+
 def _batch(seed, dt, lens, H=8, D=128, **kw):
     return W.make_decode(seed, dt, H, D, lens, **kw)
 
