@@ -121,8 +121,17 @@ struct DetectLds {
   int win[DET_CAP], lead[DET_CAP], mask[DET_CAP], lim[DET_CAP], J[DET_CAP];
   int ncand, maxlim;
 };
+// Batches of up to PLAN_SEQ_CAP sequences (one detection pass) keep each
+// sequence's clamped context length, first block id and first own token, and
+// each window's win_info, in the plan workgroup's LDS: one round trip to memory
+// fills them, and detection and classification then read LDS.  Larger batches
+// read memory each time.
+constexpr int PLAN_SEQ_CAP = DET_CAP * SHARE_WINDOW;
+struct PlanSeqLds {
+  int ctx[PLAN_SEQ_CAP], first[PLAN_SEQ_CAP], start[PLAN_SEQ_CAP], winfo[DET_CAP];
+};
 
-__device__ void detect_all(const DecodeArgs& a, DetectLds& d) {
+__device__ void detect_all(const DecodeArgs& a, DetectLds& d, PlanSeqLds& L, bool cached) {
   constexpr int GW = SHARE_WINDOW;
   const int BS = a.block_size;
   const int tid = threadIdx.x;
@@ -140,8 +149,9 @@ __device__ void detect_all(const DecodeArgs& a, DetectLds& d) {
 #pragma unroll
       for (int i = 0; i < GW; ++i) {
         const int s = s0 + i;
-        nfull[i] = s < a.num_seqs ? max(clamp_ctx(a, s), 0) / BS : 0;
-        first[i] = s < a.num_seqs ? a.block_tables[(int64_t)s * a.max_blocks_per_seq] : 0;
+        const int ctx = s < a.num_seqs ? (cached ? L.ctx[s] : clamp_ctx(a, s)) : 0;
+        nfull[i] = max(ctx, 0) / BS;
+        first[i] = s < a.num_seqs ? (cached ? L.first[s] : a.block_tables[(int64_t)s * a.max_blocks_per_seq]) : 0;
       }
       int lead = -1;
 #pragma unroll
@@ -174,28 +184,52 @@ __device__ void detect_all(const DecodeArgs& a, DetectLds& d) {
         atomicMax(&d.maxlim, lim);
       } else {
         a.win_info[win] = 0;
+        if (cached) L.winfo[win] = 0;
 #pragma unroll
         for (int i = 0; i < GW; ++i)
-          if (s0 + i < a.num_seqs) a.tok_start[s0 + i] = 0;
+          if (s0 + i < a.num_seqs) {
+            a.tok_start[s0 + i] = 0;
+            if (cached) L.start[s0 + i] = 0;
+          }
       }
     }
     __syncthreads();
     const int nc = d.ncand;
     const int maxlim = d.maxlim;
+    // Each thread takes up to four (window, block) pairs at once and issues all
+    // their table reads before comparing, so the reads overlap.
+    constexpr int QB = 4;
     for (int jr = 0; jr < maxlim; jr += 64) {
-      for (int q = tid; q < nc * 64; q += nthr) {
-        const int c = q >> 6;
-        const int j = jr + (q & 63);
-        if (j < d.lim[c] && j < d.J[c]) {  // d.J only shrinks; a stale read costs a redundant check
+      const int total = nc * 64;
+      for (int q0 = tid; q0 < total; q0 += QB * nthr) {
+        int lv[QB], wv[QB][GW];
+        bool act[QB];
+#pragma unroll
+        for (int u = 0; u < QB; ++u) {
+          const int q = q0 + u * nthr;
+          const int c = min(q >> 6, nc - 1);
+          const int j = jr + (q & 63);
+          // d.J only shrinks; a stale read costs a redundant check
+          act[u] = q < total && j < d.lim[c] && j < d.J[c];
           const int32_t* lrow = a.block_tables + (int64_t)d.lead[c] * a.max_blocks_per_seq;
           const int32_t* wrow = a.block_tables + (int64_t)d.win[c] * GW * a.max_blocks_per_seq;
-          const int lv = lrow[j];
+          const int mask = d.mask[c];
+          lv[u] = act[u] ? lrow[j] : 0;
+#pragma unroll
+          for (int i = 0; i < GW; ++i)
+            wv[u][i] = act[u] && ((mask >> i) & 1) ? wrow[(int64_t)i * a.max_blocks_per_seq + j] : 0;
+        }
+#pragma unroll
+        for (int u = 0; u < QB; ++u) {
+          if (!act[u]) continue;
+          const int q = q0 + u * nthr;
+          const int c = q >> 6;
           const int mask = d.mask[c];
           bool diff = false;
 #pragma unroll
           for (int i = 0; i < GW; ++i)
-            if ((mask >> i) & 1) diff |= wrow[(int64_t)i * a.max_blocks_per_seq + j] != lv;
-          if (diff) atomicMin(&d.J[c], j);
+            if ((mask >> i) & 1) diff |= wv[u][i] != lv[u];
+          if (diff) atomicMin(&d.J[c], jr + (q & 63));
         }
       }
       __syncthreads();
@@ -204,10 +238,14 @@ __device__ void detect_all(const DecodeArgs& a, DetectLds& d) {
       const int win = d.win[c], mask = d.mask[c], J = d.J[c];
       const bool grp = J >= 1;
       a.win_info[win] = grp ? (J << 4) | mask : 0;
+      if (cached) L.winfo[win] = grp ? (J << 4) | mask : 0;
 #pragma unroll
       for (int i = 0; i < GW; ++i) {
         const int s = win * GW + i;
-        if (s < a.num_seqs) a.tok_start[s] = grp && ((mask >> i) & 1) ? J * BS : 0;
+        if (s < a.num_seqs) {
+          a.tok_start[s] = grp && ((mask >> i) & 1) ? J * BS : 0;
+          if (cached) L.start[s] = grp && ((mask >> i) & 1) ? J * BS : 0;
+        }
       }
     }
     __syncthreads();
@@ -221,12 +259,24 @@ __device__ void detect_all(const DecodeArgs& a, DetectLds& d) {
 __global__ __launch_bounds__(1024) void decode_plan_kernel(const DecodeArgs a) {
   __shared__ int cnt[PLAN_BUCKETS];
   __shared__ DetectLds det;
+  __shared__ PlanSeqLds seq;
   const int BS = a.block_size;
   const int part_tokens = a.part_blocks * BS;
   const int P = a.num_parts;
   for (int i = threadIdx.x; i < PLAN_BUCKETS; i += blockDim.x) cnt[i] = 0;
-  if (a.win_info != nullptr) detect_all(a, det);  // ends with a barrier
+  const bool cached = a.num_seqs <= PLAN_SEQ_CAP;
+  if (cached) {
+    for (int s = threadIdx.x; s < a.num_seqs; s += blockDim.x) {
+      seq.ctx[s] = clamp_ctx(a, s);
+      seq.first[s] = a.win_info != nullptr ? a.block_tables[(int64_t)s * a.max_blocks_per_seq] : 0;
+      seq.start[s] = 0;
+    }
+    __syncthreads();
+  }
+  if (a.win_info != nullptr) detect_all(a, det, seq, cached);  // ends with a barrier
   __syncthreads();
+  auto ctx_of = [&](int s) { return cached ? seq.ctx[s] : clamp_ctx(a, s); };
+  auto start_of = [&](int s) { return cached ? seq.start[s] : seq_start(a, s); };
   // Pair i < npairs is (sequence i / P, partition i % P); pair npairs + j is
   // (window j / P, partition j % P) of the shared blocks.  Each gets a bucket
   // (-1: no entry) and its work-list entry.  A sequence's partition is tagged
@@ -245,7 +295,7 @@ __global__ __launch_bounds__(1024) void decode_plan_kernel(const DecodeArgs a) {
       const int j = i - npairs;
       const int win = j / P;
       const int p = j - win * P;
-      const int info = a.win_info[win];
+      const int info = cached ? seq.winfo[win] : a.win_info[win];
       if (info == 0) return;
       const int J = info >> 4;
       const int tok0 = p * part_tokens;
@@ -255,7 +305,7 @@ __global__ __launch_bounds__(1024) void decode_plan_kernel(const DecodeArgs a) {
       if (P == 1) {  // unsplit: the group unit also streams each member's own blocks
 #pragma unroll
         for (int g = 0; g < SHARE_WINDOW; ++g)
-          if ((info >> g) & 1) nb += (clamp_ctx(a, win * SHARE_WINDOW + g) + BS - 1) / BS - J;
+          if ((info >> g) & 1) nb += (ctx_of(win * SHARE_WINDOW + g) + BS - 1) / BS - J;
       }
       bucket = min(nb, PLAN_BUCKETS - 1);
       entry = (j << ENTRY_SHIFT) | ENTRY_GROUP;
@@ -263,10 +313,10 @@ __global__ __launch_bounds__(1024) void decode_plan_kernel(const DecodeArgs a) {
     }
     const int s = i / P;
     const int p = i - s * P;
-    const int ctx = clamp_ctx(a, s);
-    const int ctx_l = s > 0 ? clamp_ctx(a, s - 1) : 0;
-    const int ctx_r = s + 1 < a.num_seqs ? clamp_ctx(a, s + 1) : 0;
-    const int t0 = seq_start(a, s) + p * part_tokens;
+    const int ctx = ctx_of(s);
+    const int ctx_l = s > 0 ? ctx_of(s - 1) : 0;
+    const int ctx_r = s + 1 < a.num_seqs ? ctx_of(s + 1) : 0;
+    const int t0 = start_of(s) + p * part_tokens;
     if (ctx <= 0) {
       // One entry, in the smallest bucket, so that the output is written as NaN.
       if (p == 0) {
