@@ -35,6 +35,9 @@ The same line also carries:
   cached_prefix_prefill  requests prefilling over one cached shared prefix.
   prefill_prompt_count  the fresh prefill alone on config 5's 8 prompts and on
                 256 prompts of the same length distribution.
+  headline_sustained_1s  the headline step back to back for about a second,
+                with the GPU's shader clock sampled meanwhile (rocm-smi); the
+                8-prompt prefill gets the same sustained run and clock sample.
   block_size_sweep  the same decode at 8-, 16- and 32-token blocks (the pool's
                 bytes re-tiled, fresh shuffled tables).
   decode_launch_shape  the headline decode at 1, 2 and 4 workgroups per CU.
@@ -243,6 +246,19 @@ def main() -> int:
             "traffic": None if traffic is None else int(traffic),
         },
     }
+    # The same step back to back for about a second, the shader clock sampled
+    # meanwhile (context for the prefill's clock under its matrix work).
+    with _ClockSampler() as clk:
+        t_end, n_sus = time.perf_counter() + 1.0, 0
+        t1 = time.perf_counter()
+        while time.perf_counter() < t_end:
+            for _ in range(5):
+                step()
+            n_sus += 5
+            torch.cuda.synchronize()
+        sus_wall = time.perf_counter() - t1
+    line["headline_sustained_1s"] = {"steps": n_sus, "ms_per_step": round(sus_wall * 1e3 / n_sus, 4),
+                                     "sclk_MHz": clk.summary()}
     line["config3_as_written"] = config3_as_written(a, t, d)
     line["read_probe"] = read_probe(a, t, d, k_dec)
     if not a.no_extras:
@@ -409,6 +425,21 @@ def mixed_step(a, dev, up):
     w_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / n
     p_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / n
     d_ms = sum(e[2].elapsed_time(e[3]) for e in evs) / n
+    # The same step after about a second of back-to-back steps: the GPU's power
+    # management settles within tens of milliseconds of sustained matrix work,
+    # and the first launches of a burst land in its transient.
+    with _ClockSampler() as clk:
+        t_end = time.perf_counter() + 1.0
+        while time.perf_counter() < t_end:
+            for _ in range(5):
+                run()
+            torch.cuda.synchronize()
+        evs2 = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n)]
+        for e in evs2:
+            run(e)
+        torch.cuda.synchronize()
+    sus = {k: sum(e[i].elapsed_time(e[i + 1]) for e in evs2) / n for i, k in
+           enumerate(("kv_cache_write", "paged_attn_prefill", "paged_attn_decode"))}
     # The same step with the prefill (matrix cores) on a second stream, running
     # beside the write and the decode (HBM); they share no buffer.  Both
     # streams keep the default priority.
@@ -450,6 +481,13 @@ def mixed_step(a, dev, up):
         "prefill_mfma_frac": round(flops / (p_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
         "decode_GBps": round(dec_bytes / (d_ms * 1e-3) / 1e9, 1),
         "decode_tokens_attended_per_s": round(float(d.context_lens.sum()) / (d_ms * 1e-3), 1),
+        "after_1s_of_steps": {
+            "kernels_ms": {k: round(v, 5) for k, v in sus.items()},
+            "prefill_TFLOPs": round(flops / (sus["paged_attn_prefill"] * 1e-3) / 1e12, 1),
+            "prefill_mfma_frac": round(flops / (sus["paged_attn_prefill"] * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+            "decode_GBps": round(dec_bytes / (sus["paged_attn_decode"] * 1e-3) / 1e9, 1),
+            "sclk_MHz": clk.summary(),
+        },
     }
 
 
@@ -599,6 +637,47 @@ def cached_prefix_prefill(a, dev, up):
     }
 
 
+class _ClockSampler:
+    """Samples the GPU's shader clock (rocm-smi --showclocks, a child process)
+    about ten times a second while the with-block runs; None when rocm-smi is
+    not there or prints no clock."""
+
+    def __init__(self):
+        self.samples, self._stop, self._th = [], False, None
+
+    def _run(self):
+        import subprocess
+
+        while not self._stop:
+            try:
+                r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=5)
+                card = json.loads(r.stdout[r.stdout.index("{"):])
+                for v in card.values():
+                    self.samples.append(int(str(v["sclk clock speed:"]).strip("()Mhz")))
+                    break
+            except Exception:
+                return
+            time.sleep(0.05)
+
+    def __enter__(self):
+        import threading
+
+        self._th = threading.Thread(target=self._run, daemon=True)
+        self._th.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop = True
+        self._th.join(timeout=10)
+        return False
+
+    def summary(self):
+        xs = self.samples
+        if not xs:
+            return None
+        return {"min": min(xs), "mean": round(sum(xs) / len(xs)), "max": max(xs), "samples": len(xs)}
+
+
 def prefill_prompt_count(a, dev, up):
     """The fresh prefill alone (HIP events, inputs resident and warm): config 5's
     8 prompts, and 256 prompts drawn from the same length distribution
@@ -629,11 +708,32 @@ def prefill_prompt_count(a, dev, up):
         out = torch.empty((T, H, D), dtype=torch.bfloat16, device=dev)
         lens = up(L.astype(np.int32))
         steps = a.steps if T < 20000 else max(3, a.steps // 10)
-        ms = _time_events(lambda: ops.paged_attn_prefill(q, k, v, None, lens, out, max_prompt_len=int(L.max())),
-                          max(1, a.warmup // 2), steps)
+        def call():
+            ops.paged_attn_prefill(q, k, v, None, lens, out, max_prompt_len=int(L.max()))
+
+        ms = _time_events(call, max(1, a.warmup // 2), steps)
         flops = 4.0 * D * H * float((L * (L + 1) // 2).sum())
         res[name] = {"tokens": T, "ms": round(ms, 4), "TFLOPs": round(flops / (ms * 1e-3) / 1e12, 1),
                      "mfma_frac": round(flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
+        if from_workload:
+            # The same launch back to back for about a second, with the shader
+            # clock sampled meanwhile: the matrix work runs at the clock the
+            # power management grants, below the 2.4 GHz the peak assumes.
+            with _ClockSampler() as clk:
+                t_end = time.perf_counter() + 1.0
+                n_sus, e0, e1 = 0, torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                while time.perf_counter() < t_end:
+                    for _ in range(20):
+                        call()
+                    n_sus += 20
+                    torch.cuda.synchronize()
+                e1.record()
+                torch.cuda.synchronize()
+            sus_ms = e0.elapsed_time(e1) / n_sus
+            res[name]["sustained_1s"] = {"launches": n_sus, "ms": round(sus_ms, 4),
+                                         "TFLOPs": round(flops / (sus_ms * 1e-3) / 1e12, 1),
+                                         "sclk_MHz": clk.summary()}
         del q, k, v, out
     res["tflops_256_over_8"] = round(res["256_prompts"]["TFLOPs"] / res["8_prompts"]["TFLOPs"], 4)
     return res
