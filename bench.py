@@ -21,8 +21,8 @@ The same line also carries:
                 counter summary, if it was taken on this kernel source.
   cpu_baseline  the float64 CPU oracle as it stands, on the host's cores (one
                 process per core) and on one thread, over a time-boxed sample
-                of the same step's sequences; and its prefill on config 5's
-                prompts.
+                of the same step's sequences; and its prefill on the mixed
+                step's 8 prompts.
   mixed_step    the mixed prefill+decode step (8 prompts prefilled while 192
                 sequences decode), per kernel, with prefill's MFMA rate; and
                 the same step with the prefill on a second stream beside the
@@ -33,7 +33,7 @@ The same line also carries:
                 through paged_attn_decode (which reads shared blocks once) and
                 through the two-stage form (which does not).
   cached_prefix_prefill  requests prefilling over one cached shared prefix.
-  prefill_prompt_count  the fresh prefill alone on config 5's 8 prompts and on
+  prefill_prompt_count  the fresh prefill alone on the mixed step's 8 prompts and on
                 256 prompts of the same length distribution.
   headline_sustained_1s  the headline step back to back for about a second,
                 with the GPU's shader clock sampled meanwhile (rocm-smi); the
@@ -679,8 +679,8 @@ class _ClockSampler:
 
 
 def prefill_prompt_count(a, dev, up):
-    """The fresh prefill alone (HIP events, inputs resident and warm): config 5's
-    8 prompts, and 256 prompts drawn from the same length distribution
+    """The fresh prefill alone (HIP events, inputs resident and warm): the mixed
+    step's 8 prompts, and 256 prompts drawn from the same length distribution
     (U[128, 2048]), which take the enumeration for more than 64 prompts.  Both
     32 heads x 128, bf16.  q/k/v of the 256-prompt batch are drawn on the device
     (seeded); only the timing is used."""
@@ -691,7 +691,7 @@ def prefill_prompt_count(a, dev, up):
     from paged_kv_cache_137_amd import workloads as W
 
     H, D = 32, 128
-    res = {"workload": "fresh causal prefill alone, 32 heads x 128, bf16: config 5's 8 prompts, and 256 prompts "
+    res = {"workload": "fresh causal prefill alone, 32 heads x 128, bf16: the mixed step's 8 prompts, and 256 prompts "
                        "with lengths U[128, 2048]"}
     p5 = W.mixed_config(poison=False).prefill
     g = torch.Generator(device=dev)
@@ -945,7 +945,7 @@ def cpu_baseline(d, p, seconds: float, max_workers: int = 16):
     a share of 16).
 
     Decode: whole sequences of the headline step (the oracle's paged_decode on
-    one sequence), in order, wrapping round.  Prefill: config 5's prompts in
+    one sequence), in order, wrapping round.  Prefill: the mixed step's 8 prompts in
     units of (prompt, 4 heads), the oracle's causal_prefill on each.  Each leg
     runs about seconds / 4.  The one-thread legs are time-boxed; the all-core
     legs map a fixed list of units, sized from the one-thread rate, over a
@@ -1007,7 +1007,7 @@ def cpu_baseline(d, p, seconds: float, max_workers: int = 16):
             "sample": f"{dec1[0]} whole-sequence decodes ({dec1[1]} tokens, {dec1[2]:.1f} s), BLAS limited to 1 thread",
         },
         "prefill": {
-            "workload": "config 5's 8 prompts (32 heads x 128, bf16 inputs), causal, float64 oracle, in units of "
+            "workload": "the mixed step's 8 prompts (32 heads x 128, bf16 inputs), causal, float64 oracle, in units of "
                         "(prompt, 4 heads)",
             "all_cores_GFLOPs": round(fl_all / pre_all / 1e9, 3), "all_cores_units": npf,
             "all_cores_seconds": round(pre_all, 2), "cores": cores,
