@@ -197,10 +197,11 @@ int pkv_decode_partition_for_lengths(const int32_t* context_lens, int32_t num_se
  *   scale         multiplies q.k before the softmax (usually 1/sqrt(head_dim))
  *   out           [num_seqs][num_heads][head_dim] of out_dtype (PKV_F32 or desc->dtype)
  *   partition_size  tokens per context partition: a multiple of the block size,
- *                 between 16 and 4096, or 0 for no split.  Each (sequence, head, partition)
- *                 is one workgroup.  A sequence spanning more than one partition
- *                 is merged by a second, reduce kernel (max-rescaled sum of the
- *                 partial results), in a fixed order.
+ *                 between 16 and 4096, or 0 for no split.  Each (sequence,
+ *                 partition, four consecutive heads) is one unit of work.  A
+ *                 sequence spanning more than one partition is merged by a
+ *                 second, reduce kernel (max-rescaled sum of the partial
+ *                 results), in a fixed order.
  *                 PKV_PARTITION_AUTO picks the size from the shape alone
  *                 (num_seqs, num_heads, max_context_len).  With units =
  *                 num_seqs * ceil(num_heads / 4): no split when units >= 1024
