@@ -15,13 +15,27 @@ import platform
 
 
 def _cpu_model() -> str:
+    """The host CPU as /proc/cpuinfo describes it: model name, family / model /
+    stepping, clock and cache (a virtual machine may report a generic name)."""
+    info = {}
     try:
         for ln in open("/proc/cpuinfo"):
-            if ln.startswith("model name"):
-                return ln.split(":", 1)[1].strip()
+            if ":" in ln:
+                k, v = ln.split(":", 1)
+                info.setdefault(k.strip(), v.strip())
+            elif info:
+                break  # the first processor's block is enough
     except OSError:
-        pass
-    return platform.processor() or "unknown"
+        return platform.processor() or "unknown"
+    parts = [info.get("model name", platform.processor() or "unknown")]
+    ids = [f"{k} {info[k]}" for k in ("cpu family", "model", "stepping") if k in info]
+    if ids:
+        parts.append("(" + ", ".join(ids) + ")")
+    if "cpu MHz" in info:
+        parts.append(f"{float(info['cpu MHz']):.0f} MHz")
+    if "cache size" in info:
+        parts.append(f"cache {info['cache size']}")
+    return " ".join(parts)
 
 
 def host_info() -> dict:
