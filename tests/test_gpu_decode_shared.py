@@ -221,3 +221,44 @@ def test_shared_decode_bad_id_poisons_its_group_only():
     ref = oracle.attention.paged_decode(d.q, d.k_cache, d.v_cache, d.block_tables, d.context_lens, d.scale,
                                         d.dtype, block_size=d.block_size, seqs=rest)
     assert float(np.abs(got[rest] - ref[rest]).max()) <= TOL[d.dtype]
+
+
+def test_large_batch_beyond_the_plans_lds_copy():
+    """4,500 sequences: more than the plan keeps in LDS (4,096), more windows
+    than one sharing-search pass takes (1,024), and more units than one
+    classification batch.  Every third window's four sequences share their
+    first two blocks (parallel samples); the decode finds exactly those groups
+    (read back from the workspace) and matches the oracle on every sequence,
+    in the one-call and the two-stage form."""
+    print("decode, 4,500 sequences", flush=True)
+    S, H, D, B = 4500, 4, 64, 16
+    lens = np.array([33 + (37 * i) % 90 for i in range(S)], np.int32)
+    d = W.make_decode(91, "f16", H, D, lens)
+    tables = d.block_tables.copy()
+    expect = np.zeros(S, np.int32)
+    for w0 in range(0, S - WINDOW + 1, 3 * WINDOW):
+        tables[w0 + 1: w0 + WINDOW, :2] = tables[w0, :2]  # every member holds >= 2 full blocks
+        expect[w0: w0 + WINDOW] = 2 * B
+    d.block_tables = tables
+    t = upload_decode(d)
+    ref = oracle.attention.paged_decode(d.q, d.k_cache, d.v_cache, d.block_tables, d.context_lens, d.scale, d.dtype,
+                                        block_size=d.block_size)
+
+    def check(out):
+        got = down(out)
+        assert np.isfinite(got).all()
+        err = float(np.abs(got - ref).max())
+        print(f"  max|err|={err:.3e}", flush=True)
+        assert err <= TOL[d.dtype]
+
+    for part in (0, 32):
+        ws = torch.empty(ops.decode_workspace_bytes(S, H, D, d.max_context_len, part), dtype=torch.uint8,
+                         device="cuda")
+        check(_run_shared(t, d, partition_size=part, workspace=ws))
+        np.testing.assert_array_equal(_starts_from_workspace(ws, S, H, D, d.max_context_len, part), expect)
+        two = nan_out(d.q.shape, "f32")
+        kw = dict(max_context_len=d.max_context_len, partition_size=part, workspace=ws)
+        args = (t["q"], t["k_cache"], t["v_cache"], t["block_tables"], t["context_lens"], d.scale, two)
+        ops.paged_attn_decode_partial(*args, **kw)
+        ops.paged_attn_decode_reduce(*args, **kw)
+        check(two)
