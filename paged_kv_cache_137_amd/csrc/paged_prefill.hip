@@ -36,7 +36,9 @@
 //    maximum rises by more than 8 (log2 units).  Probabilities then stay below
 //    2^8, and the 64-value accumulator rescale is rare.
 //  - Causality: key tiles past the workgroup's last query are never loaded.
-//    Key tiles past a wave's last query are skipped by that wave.  Tiles that
+//    Key tiles past a wave's last query are skipped by that wave, and a wave
+//    whose queries all lie past the prompt end (in a prompt's last, partial
+//    query tile) multiplies nothing: it only loads and waits.  Tiles that
 //    straddle the diagonal or the prompt end are masked by selecting -inf.
 //  - Query tiles are dispatched longest first, to even out the causal
 //    triangle's load: prompts in order of context length (up to 64 prompts,
@@ -405,6 +407,7 @@ __global__ __launch_bounds__(256, 3) void prefill_kernel(const PrefillArgs a) {
 
   const int kend = C + min(L, m0 + BM);     // keys any query of the workgroup sees
   const int wkend = C + min(L, qrow0 + 32); // keys any query of this wave sees
+  const bool act = qrow0 < L;                // the wave holds at least one query
 
   // One tile of BN keys from LDS buffer `buf`, starting at key n0, as U
   // sub-tiles of 32 keys whose score chains are independent (with U > 1 their
@@ -504,7 +507,7 @@ __global__ __launch_bounds__(256, 3) void prefill_kernel(const PrefillArgs a) {
   auto step = [&](auto masked_c, auto buf_c, int tt) __attribute__((always_inline)) {
     constexpr int b = decltype(buf_c)::value;
     if (tt + 1 < ntiles) gdma((tt + 1) * BN, b ^ 1);
-    if (!decltype(masked_c)::value || tt * BN < wkend) tile(masked_c, b, tt * BN);
+    if (act && (!decltype(masked_c)::value || tt * BN < wkend)) tile(masked_c, b, tt * BN);
     publish();
   };
   using B0 = std::integral_constant<int, 0>;
