@@ -179,6 +179,28 @@ def test_decode_auto_partition_bounds_long_contexts():
     assert torch.equal(auto, run_decode(ops, t, d, "f32", partition_size=2048))
 
 
+def test_decode_65536_token_context():
+    """One 65,536-token context (4,096 blocks) beside short ones, 4 heads x 128,
+    bf16.  The automatic partition, 256-token partitions (256 partial results of
+    the long sequence, past the reduce's register path) and no split at all
+    (one unit streams all 4,096 blocks) each match the oracle on every sequence;
+    the 16-bit output is the rounding of the f32 one."""
+    lens = [65536, 1, 17, 4096, 300]
+    d = _batch(79, "bf16", lens, H=4)
+    auto = ops.decode_partition(d.num_seqs, 4, d.max_context_len)
+    print(f"decode, 65,536-token context: automatic partition {auto}", flush=True)
+    assert 256 <= auto <= 2048
+    ref, t_or = timed(oracle.attention.paged_decode, d.q, d.k_cache, d.v_cache, d.block_tables, d.context_lens,
+                      d.scale, d.dtype, block_size=d.block_size)
+    print(f"  oracle {t_or:.1f} s", flush=True)
+    t = upload_decode(d)
+    for part in (ops.PARTITION_AUTO, 256, 0):
+        print(f"  partition {part}", flush=True)
+        out = run_decode(ops, t, d, "f32", partition_size=part)
+        out16 = run_decode(ops, t, d, "bf16", partition_size=part)
+        _check(d, out, out16, ref=ref)
+
+
 def test_decode_padded_tables_auto_partition():
     """Tables padded far past the contexts (512 blocks, 8,192 tokens, for
     contexts of at most 300).  The automatic rule reads max_context_len: left at
