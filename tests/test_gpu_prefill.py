@@ -46,6 +46,33 @@ def test_prefill_parity_ragged(dt, D):
             assert np.array_equal(out32[o].astype(np.float64), oracle.attention.to_f64(p.v[o], dt))
 
 
+def test_prefill_32768_token_prompt():
+    """One 32,768-token prompt beside a 5-token one, 2 heads x 128, bf16: the
+    longest query tile runs 1,024 key tiles.  Sampled rows (the first and last
+    48 of the long prompt, 96 more at random, and every row of the short one)
+    against the oracle's attention over the row's causal prefix; every output
+    written; the 16-bit output is the rounding of the f32 one."""
+    lens = [32768, 5]
+    print("prefill, 32,768-token prompt", flush=True)
+    p = W.make_prefill(83, "bf16", 2, 128, lens)
+    out32 = down(_prefill(p))
+    assert np.isfinite(out32).all()
+    q, k, v = (oracle.attention.to_f64(x, "bf16") for x in (p.q, p.k, p.v))
+    rng = np.random.default_rng(84)
+    rows = sorted(set(range(48)) | set(range(32768 - 48, 32768)) | set(rng.integers(48, 32768 - 48, 96).tolist()))
+    rows += [32768 + i for i in range(5)]
+    err = 0.0
+    for i in rows:
+        start = 0 if i < 32768 else 32768
+        for h in range(2):
+            ref = oracle.attention.attend(q[i, h], k[start:i + 1, h], v[start:i + 1, h], 1 / math.sqrt(128))
+            err = max(err, float(np.abs(out32[i, h] - ref).max()))
+    print(f"  rows={len(rows)} max|err|={err:.3e}", flush=True)
+    assert err <= TOL["bf16"]
+    outdt = down(_prefill(p, "bf16"))
+    assert np.array_equal(bits(outdt), bits(rne_to(out32, "bf16")))
+
+
 @pytest.mark.parametrize("n", [63, 64, 65])
 def test_prefill_many_prompts_dense_and_sparse_enumeration(n):
     """Up to 64 prompts the kernel enumerates only existing query tiles, ranked
