@@ -336,6 +336,39 @@ def test_cached_prefix_prefill_block_sizes(bs):
     assert np.abs(down(out) - ref).max() <= TOL[dt]
 
 
+def test_cached_prefix_prefill_long_prefix():
+    """Two requests of 200 and 77 new tokens over one 16,384-token cached prefix
+    (1,024 shared blocks, then each request's own), read through shuffled
+    tables, bf16, 4 heads x 128: every output against the oracle."""
+    print("cached-prefix prefill, 16,384-token prefix", flush=True)
+    dt, H, D, bs, C = "bf16", 4, 128, 16, 16384
+    plens = [200, 77]
+    need = [-(-(C + L) // bs) for L in plens]
+    npre = C // bs
+    nb = npre + sum(n - npre for n in need) + 8
+    perm = np.random.default_rng(9).permutation(nb).astype(np.int32)
+    tables = np.zeros((len(plens), max(need)), np.int32)
+    o = npre
+    for r, n in enumerate(need):
+        tables[r, :npre] = perm[:npre]
+        tables[r, npre:n] = perm[o:o + n - npre]
+        o += n - npre
+    kc = W.normal((69, 1), (nb, H, bs, D), dt)
+    vc = W.normal((69, 2), (nb, H, bs, D), dt)
+    T = sum(plens)
+    qn = W.normal((69, 3), (T, H, D), dt)
+    out = nan_out((T, H, D), torch.float32)
+    ops.paged_attn_prefill_cached(up(qn, dt), up(kc, dt), up(vc, dt), up(tables), up(np.full(len(plens), C, np.int32)),
+                                  up(np.asarray(plens, np.int32)), out, max_prompt_len=max(plens), max_prefix_len=C)
+    ref = oracle.attention.prefix_prefill(qn, kc, vc, tables, [C] * len(plens), plens, 1 / math.sqrt(D), dt,
+                                          block_size=bs)
+    got = down(out)
+    assert np.isfinite(got).all()
+    err = float(np.abs(got - ref).max())
+    print(f"  max|err|={err:.3e}", flush=True)
+    assert err <= TOL[dt]
+
+
 @pytest.mark.parametrize("bs,D", [(16, 128), (8, 64)])
 def test_cached_prefix_prefill_bad_id_poisons_later_queries(bs, D):
     """A table entry outside the pool is never read: every query that would see
