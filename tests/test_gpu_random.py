@@ -11,6 +11,7 @@ causal prefill over ragged prompts.
 """
 
 import math
+import os
 
 import numpy as np
 import pytest
@@ -25,6 +26,8 @@ pytestmark = pytest.mark.gpu
 
 DTYPES = ["f32", "f16", "bf16"]
 EDGE = [1, 2, 7, 8, 9, 15, 16, 17, 31, 32, 33, 255, 256, 257, 511, 512, 513, 1023, 1025]
+# PKV_RANDOM_FACTOR=n runs n times as many seeds of each kind (the default run is 1).
+FACTOR = max(1, int(os.environ.get("PKV_RANDOM_FACTOR", "1")))
 
 
 def _random_decode(seed: int) -> tuple[W.DecodeInputs, int]:
@@ -70,7 +73,7 @@ def _random_decode(seed: int) -> tuple[W.DecodeInputs, int]:
     return d, part
 
 
-@pytest.mark.parametrize("seed", range(24))
+@pytest.mark.parametrize("seed", range(24 * FACTOR))
 def test_random_decode_plain_and_shared(seed):
     d, part = _random_decode(seed)
     S = d.num_seqs
@@ -90,7 +93,7 @@ def test_random_decode_plain_and_shared(seed):
         assert err <= TOL[d.dtype]
 
 
-@pytest.mark.parametrize("seed", range(16))
+@pytest.mark.parametrize("seed", range(16 * FACTOR))
 def test_random_cached_prefix_prefill(seed):
     rng = np.random.default_rng(3000 + seed)
     dt = ["f16", "bf16"][seed % 2]
@@ -133,7 +136,7 @@ def test_random_cached_prefix_prefill(seed):
     assert err <= TOL[dt]
 
 
-@pytest.mark.parametrize("seed", range(8))
+@pytest.mark.parametrize("seed", range(8 * FACTOR))
 def test_random_prefill(seed):
     rng = np.random.default_rng(5000 + seed)
     dt = ["f16", "bf16"][seed % 2]
