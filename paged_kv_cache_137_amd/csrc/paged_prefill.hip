@@ -35,6 +35,12 @@
 //    what was accumulated.  The reference maximum m moves only when a row's
 //    maximum rises by more than 8 (log2 units).  Probabilities then stay below
 //    2^8, and the 64-value accumulator rescale is rare.
+//  - Rows with few keys feel the rounding of P most: with two or three keys a
+//    bf16 probability's relative error of up to 2^-9 moves the output by up to
+//    about 2^-9 |v_1 - v_0| / 4.  So in a prompt's first key tile (the only
+//    tile of its first 32 rows) bf16 probabilities get a second, low part,
+//    bf16(P - bf16(P)), multiplied with the same V^T fragments and added to
+//    the row sum; that tile costs eight more MFMAs per wave.
 //  - Causality: key tiles past the workgroup's last query are never loaded.
 //    Key tiles past a wave's last query are skipped by that wave, and a wave
 //    whose queries all lie past the prompt end (in a prompt's last, partial
@@ -463,12 +469,19 @@ __global__ __launch_bounds__(256, 3) void prefill_kernel(const PrefillArgs a) {
     }
 
     uint32_t pk[U][8];
+    // The first key tile of a prompt holds the rows with the fewest keys, whose
+    // outputs feel the rounding of P most; there P also gets a second, low
+    // part (P - bf16(P), rounded) and a second P V product below.
+    const bool split = std::is_same_v<E, bf16_t> && MASKED && n0 == 0;
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
       for (int jj = 0; jj < 8; ++jj) {
-        pk[u][jj] = pack2<E>(fast_exp2(fmaf(st[u][2 * jj], c, -mrow)), fast_exp2(fmaf(st[u][2 * jj + 1], c, -mrow)));
+        const float p0 = fast_exp2(fmaf(st[u][2 * jj], c, -mrow)), p1 = fast_exp2(fmaf(st[u][2 * jj + 1], c, -mrow));
+        pk[u][jj] = pack2<E>(p0, p1);
         lrow = rowsum2<E>(pk[u][jj], lrow);
+        st[u][2 * jj] = p0;
+        st[u][2 * jj + 1] = p1;
       }
 
     // O^T += V^T P^T in k-steps of 16 keys.  In step (u, kk2), element i of lane
@@ -490,6 +503,33 @@ __global__ __launch_bounds__(256, 3) void prefill_kernel(const PrefillArgs a) {
           o[db] = mfma32<E>(make_uint4(lo.x, lo.y, hi.x, hi.y), pb, o[db]);
         }
       }
+    if (split) {
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+          const float h0 = __uint_as_float(pk[u][jj] << 16), h1 = __uint_as_float(pk[u][jj] & 0xffff0000u);
+          // Parts below 2^-12 of the high part are dropped: the largest
+          // probability's own rounding residue (from the FMA against the
+          // row maximum) then adds nothing, and a one-key row stays exactly v_0.
+          const float d0 = st[u][2 * jj] - h0, d1 = st[u][2 * jj + 1] - h1;
+          pk[u][jj] = pack2<E>(fabsf(d0) >= h0 * 0x1p-12f ? d0 : 0.f, fabsf(d1) >= h1 * 0x1p-12f ? d1 : 0.f);
+          lrow = rowsum2<E>(pk[u][jj], lrow);
+        }
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int kk2 = 0; kk2 < 2; ++kk2) {
+          const uint4 pb = make_uint4(pk[u][4 * kk2], pk[u][4 * kk2 + 1], pk[u][4 * kk2 + 2], pk[u][4 * kk2 + 3]);
+          const int kofs = (u * 32 + 16 * kk2) * ROWB;
+#pragma unroll
+          for (int db = 0; db < DB; ++db) {
+            const uint2 lo = lds_read_tr16(vbuf(buf) + vlane[db] + kofs);
+            const uint2 hi = lds_read_tr16(vbuf(buf) + vlane[db] + kofs + 8 * ROWB);
+            o[db] = mfma32<E>(make_uint4(lo.x, lo.y, hi.x, hi.y), pb, o[db]);
+          }
+        }
+    }
   };
 
   // Tiles below nfull hold keys that every query of the workgroup sees, all
