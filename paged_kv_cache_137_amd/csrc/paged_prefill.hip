@@ -34,7 +34,9 @@
 //    the rounded values (v_dot2 against ones), so the normalisation matches
 //    what was accumulated.  The reference maximum m moves only when a row's
 //    maximum rises by more than 8 (log2 units).  Probabilities then stay below
-//    2^8, and the 64-value accumulator rescale is rare.
+//    2^8, and the 64-value accumulator rescale is rare.  Workgroups whose rows
+//    have fewer than 256 keys (where rounding weighs most) track the maximum
+//    exactly instead, so each row's largest probability is exactly 1.
 //  - Rows with few keys feel the rounding of P most: with two or three keys a
 //    bf16 probability's relative error of up to 2^-9 moves the output by up to
 //    about 2^-9 |v_1 - v_0| / 4.  So in a prompt's first key tile (the only
@@ -413,6 +415,11 @@ __global__ __launch_bounds__(256, 3) void prefill_kernel(const PrefillArgs a) {
 
   const int kend = C + min(L, m0 + BM);     // keys any query of the workgroup sees
   const int wkend = C + min(L, qrow0 + 32); // keys any query of this wave sees
+  // Workgroups whose rows have fewer than 256 keys (a prompt's first query
+  // tile behind a prefix of under 128 tokens) track each row's maximum exactly,
+  // so that the row's largest probability is exactly 1 and free of rounding;
+  // longer rows let the maximum rise by the slack first.
+  const float slack = (C + m0 < 128) ? 0.f : RESCALE_SLACK;
   const bool act = qrow0 < L;                // the wave holds at least one query
 
   // One tile of BN keys from LDS buffer `buf`, starting at key n0, as U
@@ -457,7 +464,7 @@ __global__ __launch_bounds__(256, 3) void prefill_kernel(const PrefillArgs a) {
 #pragma unroll
       for (int j = 0; j < 16; ++j) lmax = fmaxf(lmax, st[u][j]);
     const float mt = lmax * c;  // this half's maximum over the tile, log2 units
-    if (__any(mt > mrow + RESCALE_SLACK)) {
+    if (__any(mt > mrow + slack)) {
       const float mnew = fmaxf(mrow, fmaxf(mt, __shfl_xor(mt, 32, 64)));
       const float alpha = fast_exp2(mrow - mnew);
       lrow *= alpha;
